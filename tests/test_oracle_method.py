@@ -1,0 +1,284 @@
+"""Pins for the oracle's whole all-reduce call and its error feedback.
+
+What the pages fix about the method, checked on the oracle:
+  * each value passes through the quantizer at most twice per call, for any
+    number of GPUs ([EA] Abstract; [JP] 'Echoの仕組み①', 'まとめ');
+  * the residuals the GPUs keep sum to the negated injected error ([JP]
+    'Echoの仕組み②');
+  * two moving averages of that error are added back into the next call's
+    input, so the accumulated error follows a fixed linear filter of the
+    injected errors; with gain 1 it stays within about 2.1 q instead of N q
+    ([JP] '理論保証', 'なぜ4bit通信は難しかったのか');
+  * closed forms: identical integer inputs sum exactly; zero stays zero;
+    one rank reduces to one quantize round trip.
+
+[EA] = 'Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for LLM
+Training and Inference' (abstract); [JP] = 'テンソル並列の通信を4bitに圧縮する
+「Echo」——誤差補償で精度を保ちながら分散LLMを高速化する仕組み'.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "echo_page_figures.json")))
+G = 128
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def out_to_f64(out: np.ndarray, cfg: O.Config) -> np.ndarray:
+    return bf16_to_f64(out) if cfg.out_dtype == O.OUT_BF16 else out.astype(np.float64)
+
+
+def rand_bf16(rng, n, scale=1.0, t=None):
+    v = rng.standard_t(t, size=n) if t else rng.normal(size=n)
+    return O.f32_to_bf16_bits((v * scale).astype(np.float32))
+
+
+def fresh_state(P, n, cfg=O.Config()):
+    dt = O.state_np_dtype(cfg)
+    return [np.zeros(n, dt) for _ in range(P)], [np.zeros(n, dt) for _ in range(P)]
+
+
+# --------------------------------------------------------------- at most two quantizations
+@pytest.mark.parametrize("P", [1, 2, 3, 4, 5, 8, 16])
+def test_at_most_two_quantizations_for_any_P(P):
+    fig = GOLDEN["max_quantizations_per_element"]
+    n = P * G * 2
+    rng = np.random.default_rng(P)
+    xs = [rand_bf16(rng, n) for _ in range(P)]
+    Ss, Ls = fresh_state(P, n)
+    qpass = [np.zeros(n, np.uint32) for _ in range(P)]
+    O.allreduce(O.Config(), xs, Ss, Ls, qpass=qpass)
+    seg = n // P
+    for p in range(P):
+        assert qpass[p].max() <= fig["value"]
+        own = slice(p * seg, (p + 1) * seg)
+        assert np.all(qpass[p][own] == 1)          # own contribution: only the owner's requantization
+        other = np.ones(n, bool)
+        other[own] = False
+        assert np.all(qpass[p][other] == 2)        # quantized once for the owner, once by it
+
+
+# --------------------------------------------------------------- closed forms
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+def test_identical_integer_inputs_sum_exactly(P):
+    """Every rank holds the same integers 0..15 (each group spans 0..15):
+    the payloads are lossless and the owner's sum P*v requantizes exactly."""
+    n = P * G * 4
+    rng = np.random.default_rng(10 + P)
+    k = rng.integers(0, 16, size=n)
+    k[::G] = 0
+    k[1::G] = 15
+    x = O.f32_to_bf16_bits(k.astype(np.float32))
+    xs = [x.copy() for _ in range(P)]
+    Ss, Ls = fresh_state(P, n)
+    out, _, _ = O.allreduce(O.Config(), xs, Ss, Ls)
+    assert np.array_equal(out_to_f64(out, O.Config()), P * k.astype(np.float64))
+    for p in range(P):
+        assert not Ss[p].any() and not Ls[p].any()
+
+
+def test_zero_message():
+    P, n = 4, 4 * G * 2
+    xs = [np.zeros(n, np.uint16) for _ in range(P)]
+    Ss, Ls = fresh_state(P, n)
+    out, sent, owned = O.allreduce(O.Config(), xs, Ss, Ls)
+    assert not out.any()
+    for o in range(P):
+        assert not owned[o][0].any() and not owned[o][1].any()
+    for p in range(P):
+        assert not Ss[p].view(np.uint32).any() and not Ls[p].view(np.uint32).any()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_single_rank_is_one_round_trip(bits):
+    cfg = O.Config(bits=bits, out_dtype=O.OUT_F32)
+    n = G * 8
+    rng = np.random.default_rng(20)
+    x = rand_bf16(rng, n, t=4)
+    Ss, Ls = fresh_state(1, n)
+    out, _, owned = O.allreduce(cfg, [x], Ss, Ls)
+    xf = bf16_to_f64(x).astype(np.float32)
+    for gi in range(n // G):
+        sl = slice(gi * G, (gi + 1) * G)
+        q, sb, zb, deq = O.quantize_group(xf[sl], bits)
+        assert np.array_equal(out[sl], deq)
+        assert owned[0][1][gi] == (sb | (zb << 16))
+
+
+# --------------------------------------------------------------- residuals sum to -e
+@pytest.mark.parametrize("P,bits,out_dtype", [(2, 4, O.OUT_BF16), (4, 4, O.OUT_BF16),
+                                              (8, 4, O.OUT_F32), (8, 8, O.OUT_BF16),
+                                              (16, 4, O.OUT_BF16)])
+def test_residuals_sum_to_negated_injected_error(P, bits, out_dtype):
+    """With the short memory taking the whole residual and no decay
+    (beta_short = 0, mix = 0), S' = r exactly, so the residuals are visible.
+    The injected error is e = o - sum_p x_p (state starts at zero, so the
+    feedback-added input equals x).  Sum_p r_p must equal -e up to the fp32
+    rounding of the owner's sum and of the residuals."""
+    cfg = O.Config(bits=bits, out_dtype=out_dtype, beta_short=0.0, mix_long=0.0)
+    n = P * G * 4
+    rng = np.random.default_rng(30 + P + bits)
+    xs = [rand_bf16(rng, n, t=4) for _ in range(P)]
+    Ss, Ls = fresh_state(P, n)
+    out, _, _ = O.allreduce(cfg, xs, Ss, Ls)
+    xsum = sum(bf16_to_f64(x) for x in xs)
+    e = out_to_f64(out, cfg) - xsum
+    rsum = sum(S.astype(np.float64) for S in Ss)
+    abs_terms = sum(np.abs(bf16_to_f64(x)) for x in xs) + np.abs(xsum) + np.abs(e)
+    tol = (2 * P + 2) * 2.0 ** -24 * abs_terms
+    assert np.all(np.abs(rsum + e) <= tol)
+    assert np.abs(e).max() > 100 * tol.max()        # the identity is not trivially satisfied
+
+
+# --------------------------------------------------------------- chained calls
+def run_chain(cfg, P, n, sites, inputs):
+    """Chain of `sites` calls with the state carried.  inputs(site) -> list of
+    P bf16 arrays.  Returns per-site arrays (o - sum x, feedback sum F before
+    the call), all in fp64."""
+    Ss, Ls = fresh_state(P, n, cfg)
+    d, F = [], []
+    for k in range(sites):
+        xs = inputs(k)
+        F.append(sum(S.astype(np.float64) + Lm.astype(np.float64) for S, Lm in zip(Ss, Ls))
+                 if cfg.state_dtype == O.STATE_F32 else
+                 sum(bf16_to_f64(S) + bf16_to_f64(Lm) for S, Lm in zip(Ss, Ls)))
+        out, _, _ = O.allreduce(cfg, xs, Ss, Ls)
+        d.append(out_to_f64(out, cfg) - sum(bf16_to_f64(x) for x in xs))
+    return np.array(d), np.array(F)
+
+
+def filter_weights(cfg, m):
+    """Share of an error injected m calls ago still present in the feedback:
+    T_m = (1 - mix) bS^m + mix bL^m (the two memories are normalized moving
+    averages that take shares 1 - mix and mix of each residual)."""
+    return (1 - cfg.mix_long) * cfg.beta_short ** m + cfg.mix_long * cfg.beta_long ** m
+
+
+@pytest.mark.parametrize("eta", [1.0, 0.5])
+def test_accumulated_error_follows_the_feedback_filter(eta):
+    """A_N = sum_k (o_k - sum_p x_pk) must equal sum_k [1 - eta(1 - T_{N-k})] e_k
+    where e_k = o_k - sum_p v_pk is the error injected at call k."""
+    cfg = O.Config(eta=eta)
+    P, n, sites = 4, 4 * G * 8, 56
+    rng = np.random.default_rng(40)
+    seqs = [[rand_bf16(rng, n, t=4) for _ in range(P)] for _ in range(sites)]
+    d, F = run_chain(cfg, P, n, sites, lambda k: seqs[k])
+    e = d - eta * F                       # o_k - sum_p (x_pk + eta (S + L))
+    A = np.cumsum(d, axis=0)
+    scale = np.abs(e).max()
+    for N in range(1, sites + 1):
+        c = np.array([1 - eta * (1 - filter_weights(cfg, N - 1 - k)) for k in range(N)])
+        pred = (c[:, None] * e[:N]).sum(axis=0)
+        assert np.abs(A[N - 1] - pred).max() <= 1e-5 * scale, N
+
+
+def test_bound_with_gain_one():
+    """With eta = 1 the accumulated error stays within the stated factor of
+    the per-call error at every depth; the filter's total weight
+    (1-mix)/(1-bS) + mix/(1-bL) equals that factor under this repository's
+    decays 0.5 / 0.9 and long-memory share 1/80."""
+    fig = GOLDEN["accumulated_error_bound_factor_eta1"]
+    cfg = O.Config(eta=fig["eta"])
+    total = (1 - cfg.mix_long) / (1 - cfg.beta_short) + cfg.mix_long / (1 - cfg.beta_long)
+    assert total == pytest.approx(fig["value"], abs=1e-12)
+    P, n, sites = 4, 4 * G * 8, GOLDEN["depth_example_sites"]["value"]
+    rng = np.random.default_rng(50)
+    seqs = [[rand_bf16(rng, n, t=4) for _ in range(P)] for _ in range(sites)]
+    d, F = run_chain(cfg, P, n, sites, lambda k: seqs[k])
+    e = d - F
+    A = np.cumsum(d, axis=0)
+    q = np.abs(e).max(axis=0)             # per-element size of one call's error
+    assert np.all(np.abs(A) <= fig["value"] * q * (1 + 1e-5))
+
+
+def test_uncompensated_error_grows_as_N_q():
+    """eta = 0 and the same input at every call: every call injects the same
+    error, so A_N = N e_1 exactly; the improvement of the 2.1 q bound at the
+    pages' depth of 56 is the stated ~27x."""
+    P, n, sites = 4, 4 * G * 4, GOLDEN["depth_example_sites"]["value"]
+    rng = np.random.default_rng(60)
+    xs = [rand_bf16(rng, n, t=4) for _ in range(P)]
+    d, F = run_chain(O.Config(eta=0.0), P, n, sites, lambda k: xs)
+    assert np.all(d == d[0])                      # bit-identical outputs at every call
+    A = np.cumsum(d, axis=0)
+    assert np.array_equal(A[-1], sites * d[0])
+    ratio = sites / GOLDEN["accumulated_error_bound_factor_eta1"]["value"]
+    assert round(ratio) == GOLDEN["improvement_at_56_sites"]["value"]
+    # with feedback the same repeated input stays bounded
+    d1, F1 = run_chain(O.Config(eta=1.0), P, n, sites, lambda k: xs)
+    e1 = d1 - F1
+    A1 = np.cumsum(d1, axis=0)
+    assert np.all(np.abs(A1) <= 2.1 * np.abs(e1).max(axis=0) * (1 + 1e-5))
+    assert np.abs(A[-1]).mean() > 10 * np.abs(A1[-1]).mean()
+
+
+def test_independent_errors_without_feedback_grow_as_sqrt_N():
+    P, n, sites = 4, 4 * G * 16, 56
+    rng = np.random.default_rng(70)
+    seqs = [[rand_bf16(rng, n) for _ in range(P)] for _ in range(sites)]
+    d, _ = run_chain(O.Config(eta=0.0), P, n, sites, lambda k: seqs[k])
+    A = np.cumsum(d, axis=0)
+    growth = np.sqrt((A[-1] ** 2).mean() / (d ** 2).mean())
+    assert 0.8 * np.sqrt(sites) < growth < 1.2 * np.sqrt(sites)
+
+
+# --------------------------------------------------------------- storage variants
+def test_bf16_state_stores_the_rounded_fp32_update():
+    """A compact state keeps bf16(RNE) of the value the fp32 state would hold;
+    from the same (bf16-representable) starting state one call agrees."""
+    P, n = 4, 4 * G * 4
+    rng = np.random.default_rng(80)
+    xs = [rand_bf16(rng, n, t=4) for _ in range(P)]
+    s0 = [O.f32_to_bf16_bits((0.05 * rng.normal(size=n)).astype(np.float32)) for _ in range(P)]
+    l0 = [O.f32_to_bf16_bits((0.05 * rng.normal(size=n)).astype(np.float32)) for _ in range(P)]
+    cf = O.Config()
+    cb = O.Config(state_dtype=O.STATE_BF16)
+    Sf = [bf16_to_f64(s).astype(np.float32) for s in s0]
+    Lf = [bf16_to_f64(s).astype(np.float32) for s in l0]
+    Sb = [s.copy() for s in s0]
+    Lb = [s.copy() for s in l0]
+    out_f, _, _ = O.allreduce(cf, xs, Sf, Lf)
+    out_b, _, _ = O.allreduce(cb, xs, Sb, Lb)
+    assert np.array_equal(out_f, out_b)
+    for p in range(P):
+        assert np.array_equal(Sb[p], O.f32_to_bf16_bits(Sf[p]))
+        assert np.array_equal(Lb[p], O.f32_to_bf16_bits(Lf[p]))
+
+
+def test_fp16_input_matches_bf16_input_on_common_values():
+    """Values exact in both 16-bit formats give identical results."""
+    P, n = 4, 4 * G * 4
+    rng = np.random.default_rng(90)
+    vals = [np.round(rng.normal(size=n) * 64) / 16 for _ in range(P)]   # multiples of 1/16, |v| < 64
+    xb = [O.f32_to_bf16_bits(v.astype(np.float32)) for v in vals]
+    xh = [O.f32_to_f16_bits(v.astype(np.float32)) for v in vals]
+    for a, b in zip(xb, xh):
+        assert np.array_equal(bf16_to_f64(a), O.f16_bits_to_f32(b).astype(np.float64))
+    Sb, Lb = fresh_state(P, n)
+    Sh, Lh = fresh_state(P, n)
+    ob, _, _ = O.allreduce(O.Config(), xb, Sb, Lb)
+    oh, _, _ = O.allreduce(O.Config(in_dtype=O.IN_F16), xh, Sh, Lh)
+    assert np.array_equal(ob, oh)
+    for p in range(P):
+        assert np.array_equal(Sb[p], Sh[p]) and np.array_equal(Lb[p], Lh[p])
+
+
+def test_payload_ratio_matches_the_stated_ceiling():
+    """4-bit codes plus one fp16 scale and one fp16 zero per 128 elements
+    carry 16 / (4 + 32/128) = 3.76x fewer bits than 16-bit values, the ~3.8x
+    cap the pages state for the 4-bit gain."""
+    fig = GOLDEN["speedup_ceiling_4bit"]
+    payload_bits = 4 + 32 / G
+    assert round(16 / payload_bits, 1) == fig["value"]
+    # and the oracle's payload really is that size
+    seg = G * 16
+    codes, params = O.new_payload(O.Config(), seg)
+    assert (codes.nbytes + params.nbytes) * 8 / seg == payload_bits
