@@ -1,0 +1,264 @@
+#!/usr/bin/env python3
+"""Benchmark one GPU's share of an Echo all-reduce call.
+
+A step is one rank's share of one call, i.e. the whole hot path on one GPU:
+  entry pass (feedback-add + quantize the P-1 non-owned segments + state),
+  owner pass (dequantize P-1 incoming payloads + fp32 sum + requantize +
+  state), dequantize pass (P gathered payloads -> 16-bit output).
+The other P-1 ranks are simulated on the same device: their payloads are
+produced by the same library before timing.  Inputs are resident in HBM.
+
+value = effective all-reduce bandwidth = 2 bytes * n / step time (16-bit
+input bytes per second), the metric the method is quoted on; hbm_frac is
+the algorithmic bytes per step over MI355X's 8 TB/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+       python bench.py --copy-calibration BYTES     (plain copy for PMC scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0     # MI355X HBM3E, AMD's published peak
+METRIC = "effective all-reduce GB/s per GPU (16-bit input bytes/s) and % of HBM peak"
+KERNELS = ("k_quant_feedback", "k_owner_reduce_requant", "k_dequant_gather")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def payload_bytes_per_elem(bits: int, group: int = 128) -> float:
+    return bits / 8 + 4 / group
+
+
+def algorithmic_bytes(P: int, n: int, bits: int, state_bytes: int, in_bytes=2, out_bytes=2):
+    """Bytes each kernel must move per launch (one rank's share):
+    entry: (P-1)/P of x, S and L read, S and L written, P-1 payloads written;
+    owner: 1/P of x, S, L read and S, L written, P-1 payloads read, one written;
+    gather: P payloads read, n outputs written."""
+    seg = n // P
+    pb = payload_bytes_per_elem(bits)
+    st = 4 * state_bytes   # S and L, read and written
+    k1 = (P - 1) * seg * (in_bytes + st + pb)
+    k2 = seg * (in_bytes + st + (P - 1) * pb + pb)
+    k3 = n * (pb + out_bytes)
+    return {"k_quant_feedback": k1, "k_owner_reduce_requant": k2, "k_dequant_gather": k3}
+
+
+def kernel_source_digest() -> str:
+    """Digest of everything that determines the kernels' code."""
+    from error_compensated_bit_amd import build as eb
+    h = hashlib.sha256()
+    for f in eb.SOURCES + eb.HEADERS:
+        h.update(open(f, "rb").read())
+    h.update(" ".join(eb.hipcc_flags()).encode())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str, kernel: str):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE,
+    scaled by the same counters on a plain copy of known size; None when no
+    summary exists or the kernels changed since it was taken."""
+    path = os.path.join(HERE, "profiles", f"pmc_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    k = d["kernels"].get(kernel)
+    c = d["copy_calibration"]
+    if not k or not c:
+        return None
+    fr = c["bytes_read"] / (c["fetch_kib"] * 1024.0)
+    fw = c["bytes_written"] / (c["write_kib"] * 1024.0)
+    return k["fetch_kib"] * 1024.0 * fr + k["write_kib"] * 1024.0 * fw
+
+
+def copy_calibration(nbytes: int):
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {nbytes} bytes read and written per launch, 3 launches")
+
+
+def cpu_baseline(cfg, w, xs_dev, frac_den: int):
+    """The CPU oracle on a bounded sample: the first 1/frac_den of every
+    segment of every rank, one call from an empty state, all P ranks.
+    One rank's share = mean entry pass + mean owner pass + one gather."""
+    import numpy as np
+    import oracle as O
+    from error_compensated_bit_amd.inputs import bits16_numpy
+    P, n = w.P, w.n
+    seg = n // P
+    sseg = seg // frac_den
+    ns = sseg * P
+    xs = []
+    for x in xs_dev:
+        xs.append(np.concatenate([bits16_numpy(x[o * seg:o * seg + sseg]) for o in range(P)]))
+    ocfg = O.Config(bits=cfg.bits, group=cfg.group, eta=cfg.eta, beta_short=cfg.beta_short,
+                    beta_long=cfg.beta_long, mix_long=cfg.mix_long, in_dtype=cfg.in_dtype,
+                    out_dtype=cfg.out_dtype, state_dtype=cfg.state_dtype)
+    Ss = [np.zeros(ns, O.state_np_dtype(ocfg)) for _ in range(P)]
+    Ls = [np.zeros(ns, O.state_np_dtype(ocfg)) for _ in range(P)]
+    sent = [[None if o == p else O.new_payload(ocfg, sseg) for o in range(P)] for p in range(P)]
+    owned = [O.new_payload(ocfg, sseg) for _ in range(P)]
+    t_entry = t_owner = 0.0
+    for p in range(P):
+        t0 = time.perf_counter()
+        O.quantize_feedback(ocfg, P, p, xs[p], Ss[p], Ls[p],
+                            [None if o == p else sent[p][o][0] for o in range(P)],
+                            [None if o == p else sent[p][o][1] for o in range(P)])
+        t_entry += time.perf_counter() - t0
+    for o in range(P):
+        t0 = time.perf_counter()
+        O.owner_reduce_requant(ocfg, P, o, xs[o], Ss[o], Ls[o],
+                               [None if p == o else sent[p][o][0] for p in range(P)],
+                               [None if p == o else sent[p][o][1] for p in range(P)],
+                               owned[o][0], owned[o][1])
+        t_owner += time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.dequant_gather(ocfg, P, ns, [c for c, _ in owned], [q for _, q in owned])
+    t_gather = time.perf_counter() - t0
+    t_share = t_entry / P + t_owner / P + t_gather
+    return {"value": round(2.0 * ns / t_share / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"first 1/{frac_den} of every segment ({ns} of {n} elements per rank), "
+                      f"all {P} ranks, one call; share time {t_share:.2f} s "
+                      f"(entry {t_entry / P:.2f} + owner {t_owner / P:.2f} + gather {t_gather:.2f}); "
+                      f"single-threaded scalar C, total CPU time "
+                      f"{t_entry + t_owner + t_gather:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="msg1gib_p8")
+    ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--state", choices=("f32", "bf16"), default="f32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-den", type=int, default=4)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the all-reduce (the other ranks are "
+              "simulated on the same device); only --gpus 1 is supported.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    from error_compensated_bit_amd import binding as B
+    from error_compensated_bit_amd import sim
+    from error_compensated_bit_amd.inputs import WORKLOADS, make_x
+
+    B.load_library()
+    w = WORKLOADS[args.workload]
+    P, n = w.P, w.n
+    bits = w.bits(0)
+    sdt = B.ECHO_STATE_F32 if args.state == "f32" else B.ECHO_STATE_BF16
+    cfg = B.make_config(bits=bits, state_dtype=sdt)
+    dev = "cuda:0"
+    log(f"workload {w.name}: {w.description}; rank {args.rank} of {P}, n={n}, bits={bits}, "
+        f"state={args.state}")
+
+    t_setup = time.perf_counter()
+    xs = [make_x(w, 0, p, device=dev) for p in range(P)]
+    r = sim.alloc_ranks(cfg, P, n, dev)
+    sim.allreduce(cfg, r, xs)          # every rank's payloads exist before timing
+    torch.cuda.synchronize()
+    log(f"setup {time.perf_counter() - t_setup:.1f} s")
+
+    rank = args.rank
+    x = xs[rank]
+    inp = [None if p == rank else r.sent[p][rank] for p in range(P)]
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        B.echo_quantize_feedback(cfg, P, rank, n, x, r.S[rank], r.L[rank], r.sent[rank], stream)
+        if ev is not None:
+            ev[1].record(stream)
+        B.echo_owner_reduce_requant(cfg, P, rank, n, x, r.S[rank], r.L[rank], inp,
+                                    r.owned[rank], stream)
+        if ev is not None:
+            ev[2].record(stream)
+        B.echo_dequant_gather(cfg, P, n, r.owned, r.out, stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    k_ms = {k: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
+            for j, k in enumerate(KERNELS)}
+    ms_per_step = wall * 1e3 / args.steps
+    alg = algorithmic_bytes(P, n, bits, 4 if sdt == B.ECHO_STATE_F32 else 2)
+    alg_total = sum(alg.values())
+    for k in KERNELS:
+        log(f"  {k:24s} {k_ms[k]:8.4f} ms  {alg[k] / k_ms[k] / 1e6:8.1f} GB/s algorithmic "
+            f"({alg[k] / k_ms[k] / 1e6 / HBM_PEAK_GBS:.1%} of HBM peak)")
+    log(f"  step {ms_per_step:.4f} ms wall, {sum(k_ms.values()):.4f} ms in kernels")
+
+    dom = max(KERNELS, key=lambda k: alg[k])
+    achieved = alg[dom] / k_ms[dom] / 1e6
+    traffic = traffic_from_profile(w.name, dom)
+    value = 2.0 * n / (ms_per_step * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_frac": round(alg_total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "config": {"workload": w.name, "P": P, "n_per_rank": n, "rank": rank, "bits": bits,
+                   "group": 128, "state": args.state, "input": "bf16", "output": "bf16",
+                   "eta": cfg.eta, "beta_short": cfg.beta_short, "beta_long": cfg.beta_long,
+                   "mix_long": round(cfg.mix_long, 6),
+                   "algorithmic_bytes_per_step": int(alg_total)},
+        "kernel_ms": {k: round(v, 5) for k, v in k_ms.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else int(traffic),
+                     "algorithmic_bytes": int(alg[dom])},
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a sample ...")
+        line["cpu_baseline"] = cpu_baseline(cfg, w, xs, args.cpu_sample_den)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

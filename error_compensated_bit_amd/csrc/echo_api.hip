@@ -1,0 +1,186 @@
+// echo_api.hip -- the C ABI declared in include/echo.h: argument validation,
+// kernel-argument marshalling and launch.  Every check runs before the first
+// HIP call, so invalid arguments are reported without touching a GPU.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "echo.h"
+#include "echo_internal.h"
+
+using echo::LaunchArgs;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_config(const echo_config* c) {
+  if (!c) return ECHO_ERR_ARG;
+  if (c->bits != 4 && c->bits != 8) return ECHO_ERR_ARG;
+  if (c->group != ECHO_GROUP) return ECHO_ERR_ARG;
+  if (c->in_dtype != ECHO_IN_BF16 && c->in_dtype != ECHO_IN_F16) return ECHO_ERR_ARG;
+  if (c->out_dtype != ECHO_OUT_BF16 && c->out_dtype != ECHO_OUT_F32) return ECHO_ERR_ARG;
+  if (c->state_dtype != ECHO_STATE_F32 && c->state_dtype != ECHO_STATE_BF16) return ECHO_ERR_ARG;
+  if (!isfinite(c->eta)) return ECHO_ERR_ARG;
+  if (!(c->beta_short >= 0.0f && c->beta_short < 1.0f)) return ECHO_ERR_ARG;
+  if (!(c->beta_long >= 0.0f && c->beta_long < 1.0f)) return ECHO_ERR_ARG;
+  if (!(c->mix_long >= 0.0f && c->mix_long <= 1.0f)) return ECHO_ERR_ARG;
+  return ECHO_OK;
+}
+
+// P ranks, message of n elements: n must be a positive multiple of P*group,
+// and a segment must fit the kernels' 32-bit group counter.
+int check_shape(int P, int64_t n) {
+  if (P < 1 || P > ECHO_MAX_RANKS) return ECHO_ERR_ARG;
+  if (n <= 0) return ECHO_ERR_SHAPE;
+  if (n % ((int64_t)P * ECHO_GROUP) != 0) return ECHO_ERR_SHAPE;
+  if (n / P / ECHO_GROUP > (int64_t)UINT32_MAX) return ECHO_ERR_SHAPE;
+  return ECHO_OK;
+}
+
+int check_buf(const void* p) {
+  if (!p) return ECHO_ERR_ARG;
+  return aligned16(p) ? ECHO_OK : ECHO_ERR_ALIGN;
+}
+
+int check_seg(const echo_seg* s) {
+  if (!s) return ECHO_ERR_ARG;
+  int rc = check_buf(s->codes);
+  if (rc) return rc;
+  return check_buf(s->params);
+}
+
+// Moving-average weights, computed in double from the float parameters and
+// rounded once: a residual r enters S with (1-bS)(1-mix) and L with (1-bL)mix.
+echo::Coef make_coef(const echo_config* c) {
+  echo::Coef k;
+  k.eta = c->eta;
+  k.bS = c->beta_short;
+  k.bL = c->beta_long;
+  k.aS = (float)((1.0 - (double)c->beta_short) * (1.0 - (double)c->mix_long));
+  k.aL = (float)((1.0 - (double)c->beta_long) * (double)c->mix_long);
+  return k;
+}
+
+LaunchArgs base_args(const echo_config* c, int P, int rank, int64_t n) {
+  LaunchArgs a;
+  memset(&a, 0, sizeof a);
+  a.bits = c->bits;
+  a.in_dtype = c->in_dtype;
+  a.out_dtype = c->out_dtype;
+  a.state_dtype = c->state_dtype;
+  a.P = P;
+  a.rank = rank;
+  a.seg_len = (uint64_t)(n / P);
+  a.coef = make_coef(c);
+  return a;
+}
+
+int launched() {
+  return hipGetLastError() == hipSuccess ? ECHO_OK : ECHO_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int echo_state_reset(const echo_config* cfg, void* S, void* L, int64_t n, void* stream) {
+  if (!cfg) return ECHO_ERR_ARG;
+  if (cfg->state_dtype != ECHO_STATE_F32 && cfg->state_dtype != ECHO_STATE_BF16) return ECHO_ERR_ARG;
+  if (n <= 0) return ECHO_ERR_ARG;
+  int rc;
+  if ((rc = check_buf(S)) || (rc = check_buf(L))) return rc;
+  const uint64_t bytes = (uint64_t)n * (cfg->state_dtype == ECHO_STATE_F32 ? 4u : 2u);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  echo::run_zero(S, bytes, st);
+  echo::run_zero(L, bytes, st);
+  return launched();
+}
+
+int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n, const void* x,
+                           void* S, void* L, const echo_seg* out, void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
+  if (rank < 0 || rank >= P) return ECHO_ERR_ARG;
+  if ((rc = check_buf(x)) || (rc = check_buf(S)) || (rc = check_buf(L))) return rc;
+  if (!out) return ECHO_ERR_ARG;
+  LaunchArgs a = base_args(cfg, P, rank, n);
+  for (int p = 0; p < P; ++p) {
+    if (p == rank) continue;
+    if ((rc = check_seg(&out[p]))) return rc;
+    a.segs.codes[p] = out[p].codes;
+    a.segs.params[p] = out[p].params;
+  }
+  if (P == 1) return ECHO_OK;  // nothing is sent when a rank owns the whole message
+  a.x = x;
+  a.S = S;
+  a.L = L;
+  echo::run_quant_feedback(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n, const void* x,
+                              void* S, void* L, const echo_seg* in, const echo_seg* out,
+                              void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
+  if (rank < 0 || rank >= P) return ECHO_ERR_ARG;
+  if ((rc = check_buf(x)) || (rc = check_buf(S)) || (rc = check_buf(L))) return rc;
+  if (!in && P > 1) return ECHO_ERR_ARG;
+  if ((rc = check_seg(out))) return rc;
+  LaunchArgs a = base_args(cfg, P, rank, n);
+  for (int p = 0; p < P; ++p) {
+    if (p == rank) continue;
+    if ((rc = check_seg(&in[p]))) return rc;
+    a.segs.codes[p] = in[p].codes;
+    a.segs.params[p] = in[p].params;
+  }
+  a.x = x;
+  a.S = S;
+  a.L = L;
+  a.out_codes = out->codes;
+  a.out_params = out->params;
+  echo::run_owner_reduce_requant(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+int echo_dequant_gather(const echo_config* cfg, int P, int64_t n, const echo_seg* in, void* out,
+                        void* stream) {
+  int rc;
+  if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
+  if (!in) return ECHO_ERR_ARG;
+  if ((rc = check_buf(out))) return rc;
+  LaunchArgs a = base_args(cfg, P, 0, n);
+  for (int p = 0; p < P; ++p) {
+    if ((rc = check_seg(&in[p]))) return rc;
+    a.segs.codes[p] = in[p].codes;
+    a.segs.params[p] = in[p].params;
+  }
+  a.out = out;
+  echo::run_dequant_gather(a, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+size_t echo_codes_bytes(int64_t seg_len, int bits) {
+  if (seg_len <= 0 || (bits != 4 && bits != 8)) return 0;
+  if (bits == 4 && seg_len % 2) return 0;
+  return (size_t)seg_len * (size_t)bits / 8;
+}
+
+size_t echo_params_bytes(int64_t seg_len, int group) {
+  if (seg_len <= 0 || group <= 0 || seg_len % group) return 0;
+  return (size_t)(seg_len / group) * sizeof(uint32_t);
+}
+
+const char* echo_error_string(int code) {
+  switch (code) {
+    case ECHO_OK: return "ok";
+    case ECHO_ERR_ARG: return "invalid argument";
+    case ECHO_ERR_SHAPE: return "message length is not a positive multiple of P * group";
+    case ECHO_ERR_ALIGN: return "buffer not 16-byte aligned";
+    case ECHO_ERR_HIP: return "HIP launch error";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

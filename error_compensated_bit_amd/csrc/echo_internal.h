@@ -1,0 +1,52 @@
+// echo_internal.h -- types shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace echo {
+
+constexpr int kGroup = 128;
+constexpr int kMaxRanks = 16;
+
+// element-type tags (same values as the ECHO_* constants of the public header)
+constexpr int kInBF16 = 0, kInF16 = 1;
+constexpr int kOutBF16 = 0, kOutF32 = 1;
+constexpr int kStateF32 = 0, kStateBF16 = 1;
+
+// Upper bound on blocks per launch; larger problems stride.
+constexpr uint64_t kGridCap = 1u << 20;
+
+// Payload pointers of every segment, passed by value as kernel arguments.
+struct SegTable {
+  void* codes[kMaxRanks];
+  uint32_t* params[kMaxRanks];
+};
+
+// Feedback gain and the two moving averages' keep/take weights.
+struct Coef {
+  float eta;
+  float bS, aS;  // short memory: S = bS*S + aS*r
+  float bL, aL;  // long memory:  L = bL*L + aL*r
+};
+
+struct LaunchArgs {
+  int bits, in_dtype, out_dtype, state_dtype;
+  int P, rank;
+  uint64_t seg_len;
+  const void* x;
+  void* S;
+  void* L;
+  SegTable segs;
+  void* out_codes;
+  uint32_t* out_params;
+  void* out;
+  Coef coef;
+};
+
+void run_quant_feedback(const LaunchArgs& a, hipStream_t st);
+void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st);
+void run_dequant_gather(const LaunchArgs& a, hipStream_t st);
+void run_zero(void* p, uint64_t bytes, hipStream_t st);
+
+}  // namespace echo

@@ -1,0 +1,167 @@
+/*
+ * echo.h -- C ABI of the Echo low-bit all-reduce hot path on one AMD
+ * Instinct gfx950 GPU: one rank's share of one all-reduce call.
+ *
+ * Echo (arXiv 2610.14277) rebuilds a tensor-parallel all-reduce as
+ * all-to-all + high-precision sum at the segment owner + all-gather, moves
+ * the data as 4-bit (or 8-bit) integers with half-precision group
+ * parameters, and feeds the error each call injects back into later calls
+ * through two moving averages.  This library holds the per-GPU compute of
+ * one call; moving the payloads between GPUs is the caller's job.
+ *
+ * Pages cited below:
+ *   [EA]   "Echo: Error-Compensated 4-Bit Tensor-Parallel Communication for
+ *          LLM Training and Inference" -- arXiv abstract.
+ *   [JP-W] "テンソル並列の通信を4bitに圧縮する「Echo」" (Japanese explainer),
+ *          section "なぜ4bit通信は難しかったのか".
+ *   [JP-1] same page, section "Echoの仕組み①" (high-precision sum, low-bit
+ *          transport, zero-point-aware asymmetric quantization).
+ *   [JP-2] same page, section "Echoの仕組み②" (dual-time-constant feedback
+ *          fused into the entry pass).
+ *   [JP-F] same page, section "よくある質問" (4-bit integers + half-precision
+ *          parameters).
+ *
+ * Layout (every call):
+ *   - A message of n elements per rank is split into P equal contiguous
+ *     segments; rank p owns segment p = [p*n/P, (p+1)*n/P).
+ *   - Groups of 128 consecutive elements of a segment share one scale and
+ *     one zero point, both IEEE binary16; params[g] = scale | zero << 16.
+ *   - Codes: bits = 4 -> two per byte, the even element in the low nibble;
+ *     bits = 8 -> one per byte.  Codes and params of a segment are two
+ *     separate arrays ("payload", echo_seg).
+ *   - Dequantized value = fma(code, scale, zero) in fp32.
+ *   - Error state: two arrays S (short memory) and L (long memory) of n
+ *     elements per rank, fp32 or bf16 (config), updated in place.
+ *
+ * Conventions:
+ *   - All buffer pointers are device pointers, 16-byte aligned; the caller
+ *     owns every buffer.  echo_config and echo_seg arrays are host memory
+ *     read during the call only.  The library allocates nothing and keeps
+ *     no state between calls; calls on different streams touching disjoint
+ *     buffers may run concurrently.
+ *   - All calls are asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream) and never synchronize.
+ *   - Payload buffers must not overlap x, S, L, the output or each other.
+ *   - Every call validates all arguments before touching the GPU and
+ *     returns ECHO_OK or a negative error code; nothing is launched when an
+ *     error is returned.  No exception crosses this interface.
+ */
+#ifndef ECHO_H
+#define ECHO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define ECHO_OK          0
+#define ECHO_ERR_ARG    -1   /* null pointer, unsupported or out-of-range parameter */
+#define ECHO_ERR_SHAPE  -2   /* n not a positive multiple of P * group */
+#define ECHO_ERR_ALIGN  -3   /* a buffer pointer is not 16-byte aligned */
+#define ECHO_ERR_HIP    -4   /* the HIP runtime reported an error at launch */
+
+/* element types */
+#define ECHO_IN_BF16     0   /* 16-bit input message: bfloat16 */
+#define ECHO_IN_F16      1   /*                       IEEE binary16 */
+#define ECHO_OUT_BF16    0   /* all-reduce output: bfloat16 (round to nearest even) */
+#define ECHO_OUT_F32     1   /*                    fp32 */
+#define ECHO_STATE_F32   0   /* error state S, L: fp32 */
+#define ECHO_STATE_BF16  1   /*                   bfloat16 (round to nearest even) */
+
+#define ECHO_MAX_RANKS  16
+#define ECHO_GROUP      128  /* the only group size the GPU path accepts */
+
+typedef struct echo_config {
+    int32_t bits;        /* 4 or 8: code width ([JP-F]; 8-bit for early sites) */
+    int32_t group;       /* elements per scale/zero pair; must be ECHO_GROUP */
+    int32_t in_dtype;    /* ECHO_IN_*    */
+    int32_t out_dtype;   /* ECHO_OUT_*   */
+    int32_t state_dtype; /* ECHO_STATE_* */
+    float   eta;         /* feedback gain; finite */
+    float   beta_short;  /* decay of the short memory, in [0, 1) */
+    float   beta_long;   /* decay of the long memory, in [0, 1) */
+    float   mix_long;    /* share of each residual given to the long memory, in [0, 1] */
+} echo_config;
+
+/* One segment's payload: codes (n/P * bits/8 bytes) and params (n/P/group words). */
+typedef struct echo_seg {
+    void*     codes;
+    uint32_t* params;
+} echo_seg;
+
+/*
+ * echo_state_reset -- empty both memories: S[j] = L[j] = +0 for j < n.
+ *   S, L: device arrays of n elements of the config's state type.
+ *   The feedback of [JP-2] carries error into later calls; a chain of calls
+ *   starts from an empty state.  Implemented as a fill kernel (no memset
+ *   node), so it may be captured in a HIP graph.
+ *   Errors: ECHO_ERR_ARG (null cfg/pointer, n <= 0, bad state type),
+ *   ECHO_ERR_ALIGN, ECHO_ERR_HIP.
+ */
+int echo_state_reset(const echo_config* cfg, void* S, void* L, int64_t n, void* stream);
+
+/*
+ * echo_quantize_feedback -- entry pass of rank `rank` ([JP-1], [JP-2]).
+ *   For every element j of every segment p != rank:
+ *     v = x[j] + eta * (S[j] + L[j])                 (fp32, unfused)
+ *   each 128-group of v is quantized to `bits` with an fp16 zero point
+ *   (the group minimum) and fp16 step ((max - zero) / (2^bits - 1)), codes
+ *   round half to even; the payload goes to out[p].  With r = v - dequant:
+ *     S[j] = beta_short * S[j] + (1-beta_short)(1-mix_long) * r
+ *     L[j] = beta_long  * L[j] + (1-beta_long) * mix_long   * r
+ *   The owned segment is not read or written (its feedback is applied by
+ *   echo_owner_reduce_requant); P = 1 launches nothing.
+ *   x: device, n 16-bit elements (in_dtype).  S, L: device, n elements.
+ *   out: host array of P echo_seg; out[rank] is ignored, every other entry
+ *   must point at a payload sized for n/P elements.
+ *   Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_ALIGN, ECHO_ERR_HIP.
+ */
+int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n,
+                           const void* x, void* S, void* L,
+                           const echo_seg* out, void* stream);
+
+/*
+ * echo_owner_reduce_requant -- owner pass of rank `rank` over its segment
+ * ([JP-1]: the owner sums in high precision and requantizes; [JP-W]).
+ *   For every element j of segment `rank`:
+ *     v_own = x[j] + eta * (S[j] + L[j])
+ *     acc   = sum over p = 0..P-1 in that order of
+ *             (p == rank ? v_own : dequant of in[p]'s code for j)    (fp32)
+ *   acc is requantized per 128-group into *out (same quantizer as above);
+ *   o = the output value of j (bf16-rounded dequant for ECHO_OUT_BF16,
+ *   the fp32 dequant for ECHO_OUT_F32); r = acc - o; S and L are updated
+ *   with r as above.  Segments p != rank are not read or written in x, S, L.
+ *   in: host array of P echo_seg (payloads the other ranks sent for this
+ *   segment); in[rank] is ignored.  out: host pointer to one echo_seg.
+ *   Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_ALIGN, ECHO_ERR_HIP.
+ */
+int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n,
+                              const void* x, void* S, void* L,
+                              const echo_seg* in, const echo_seg* out, void* stream);
+
+/*
+ * echo_dequant_gather -- turn the P owners' requantized payloads into the
+ * all-reduce output ([JP-1]: the owner's requantized sum goes to every GPU).
+ *   out[p*n/P + k] = dequant of in[p]'s code k, as out_dtype (bf16 round to
+ *   nearest even, or fp32), for every p < P and k < n/P.
+ *   in: host array of P echo_seg, all used.  out: device, n elements.
+ *   Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_ALIGN, ECHO_ERR_HIP.
+ */
+int echo_dequant_gather(const echo_config* cfg, int P, int64_t n,
+                        const echo_seg* in, void* out, void* stream);
+
+/* Payload sizes for a segment of seg_len elements (0 for invalid input). */
+size_t echo_codes_bytes(int64_t seg_len, int bits);
+size_t echo_params_bytes(int64_t seg_len, int group);
+
+/* Static description of an error code. */
+const char* echo_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ECHO_H */

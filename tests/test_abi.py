@@ -1,0 +1,110 @@
+"""The C-ABI library without a GPU: it loads, exports every function that
+include/echo.h declares, and rejects invalid arguments with the documented
+codes before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from error_compensated_bit_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "echo.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(echo_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("echo_state_reset", "echo_quantize_feedback", "echo_owner_reduce_requant",
+              "echo_dequant_gather"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load_library()
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_payload_sizes():
+    assert B.echo_codes_bytes(1024, 4) == 512
+    assert B.echo_codes_bytes(1024, 8) == 1024
+    assert B.echo_codes_bytes(1023, 4) == 0
+    assert B.echo_codes_bytes(1024, 5) == 0
+    assert B.echo_params_bytes(1024, 128) == 32
+    assert B.echo_params_bytes(1000, 128) == 0
+
+
+def test_constants_match_the_header():
+    text = open(HEADER).read()
+    for name in ("ECHO_OK", "ECHO_ERR_ARG", "ECHO_ERR_SHAPE", "ECHO_ERR_ALIGN", "ECHO_ERR_HIP",
+                 "ECHO_IN_BF16", "ECHO_IN_F16", "ECHO_OUT_BF16", "ECHO_OUT_F32",
+                 "ECHO_STATE_F32", "ECHO_STATE_BF16", "ECHO_MAX_RANKS", "ECHO_GROUP"):
+        m = re.search(rf"#define\s+{name}\s+(-?\d+)", text)
+        assert m and int(m.group(1)) == getattr(B, name), name
+    assert ctypes.sizeof(B.echo_config) == 36 and ctypes.sizeof(B.echo_seg) == 16
+
+
+# Invalid arguments: every call below must return before any HIP call (there
+# is no GPU here).  Fake, 16-byte aligned device addresses are never touched.
+A = 0x10000
+SEGS = (B.echo_seg * 16)(*[B.echo_seg(A, A) for _ in range(16)])
+
+
+def cfg(**kw):
+    return ctypes.byref(B.make_config(**kw))
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda L: L.echo_quantize_feedback(None, 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(bits=3), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(group=64), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(in_dtype=7), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(eta=float("nan")), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(beta_short=1.0), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(beta_long=-0.1), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(mix_long=1.5), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 0, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 17, 0, 17 * 128, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 2, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, -1, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 0, A, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 384, A, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, None, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A + 8, A, A, SEGS, None), B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A, A + 4, SEGS, None), B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A, A, None, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(
+        cfg(), 2, 0, 256, A, A, A, (B.echo_seg * 2)(B.echo_seg(A, A), B.echo_seg(None, A)), None),
+     B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(
+        cfg(), 2, 0, 256, A, A, A, (B.echo_seg * 2)(B.echo_seg(A, A), B.echo_seg(A, A + 2)), None),
+     B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_owner_reduce_requant(cfg(), 2, 0, 256, A, A, A, SEGS, None, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_owner_reduce_requant(cfg(), 2, 0, 256, A, A, A, None, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_owner_reduce_requant(cfg(), 4, 1, 4 * 128 * 3 + 128, A, A, A, SEGS, SEGS, None),
+     B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_owner_reduce_requant(cfg(bits=8, out_dtype=2), 2, 0, 256, A, A, A, SEGS, SEGS, None),
+     B.ECHO_ERR_ARG),
+    (lambda L: L.echo_dequant_gather(cfg(), 2, 256, None, A, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_dequant_gather(cfg(), 2, 256, SEGS, A + 1, None), B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_dequant_gather(cfg(), 2, 200, SEGS, A, None), B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_state_reset(None, A, A, 10, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_state_reset(cfg(state_dtype=5), A, A, 10, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_state_reset(cfg(), A, A, 0, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_state_reset(cfg(), A, A + 8, 10, None), B.ECHO_ERR_ALIGN),
+])
+def test_invalid_arguments_return_codes(call, code):
+    assert call(B.load_library()) == code
+
+
+def test_error_strings():
+    for c in (0, -1, -2, -3, -4, 99):
+        assert isinstance(B.error_string(c), str) and B.error_string(c)
