@@ -193,11 +193,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        B.echo_quantize_feedback(cfg, P, rank, n, x, r.S[rank], r.L[rank], r.sent[rank], stream)
+        B.echo_quantize_feedback(cfg, P, rank, n, x, r.state[rank], r.sent[rank], stream)
         if ev is not None:
             ev[1].record(stream)
-        B.echo_owner_reduce_requant(cfg, P, rank, n, x, r.S[rank], r.L[rank], inp,
-                                    r.owned[rank], stream)
+        B.echo_owner_reduce_requant(cfg, P, rank, n, x, r.state[rank], inp, r.owned[rank], stream)
         if ev is not None:
             ev[2].record(stream)
         B.echo_dequant_gather(cfg, P, n, r.owned, r.out, stream)

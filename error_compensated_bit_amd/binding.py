@@ -24,7 +24,8 @@ ECHO_MAX_RANKS = 16
 ECHO_GROUP = 128
 
 EXPORTED = ("echo_state_reset", "echo_quantize_feedback", "echo_owner_reduce_requant",
-            "echo_dequant_gather", "echo_codes_bytes", "echo_params_bytes", "echo_error_string")
+            "echo_dequant_gather", "echo_codes_bytes", "echo_params_bytes", "echo_state_bytes",
+            "echo_error_string")
 
 
 class echo_config(ctypes.Structure):
@@ -58,14 +59,16 @@ def load_library() -> ctypes.CDLL:
         L = ctypes.CDLL(path)
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
         cfgp, segp = ctypes.POINTER(echo_config), ctypes.POINTER(echo_seg)
-        L.echo_state_reset.argtypes = [cfgp, vp, vp, i64, vp]
-        L.echo_quantize_feedback.argtypes = [cfgp, i32, i32, i64, vp, vp, vp, segp, vp]
-        L.echo_owner_reduce_requant.argtypes = [cfgp, i32, i32, i64, vp, vp, vp, segp, segp, vp]
+        L.echo_state_reset.argtypes = [cfgp, vp, i64, vp]
+        L.echo_quantize_feedback.argtypes = [cfgp, i32, i32, i64, vp, vp, segp, vp]
+        L.echo_owner_reduce_requant.argtypes = [cfgp, i32, i32, i64, vp, vp, segp, segp, vp]
         L.echo_dequant_gather.argtypes = [cfgp, i32, i64, segp, vp, vp]
         L.echo_codes_bytes.argtypes = [i64, i32]
         L.echo_params_bytes.argtypes = [i64, i32]
+        L.echo_state_bytes.argtypes = [i64, i32]
         L.echo_codes_bytes.restype = ctypes.c_size_t
         L.echo_params_bytes.restype = ctypes.c_size_t
+        L.echo_state_bytes.restype = ctypes.c_size_t
         L.echo_error_string.argtypes = [i32]
         L.echo_error_string.restype = ctypes.c_char_p
         for name in ("echo_state_reset", "echo_quantize_feedback",
@@ -102,6 +105,10 @@ def echo_codes_bytes(seg_len: int, bits: int) -> int:
 
 def echo_params_bytes(seg_len: int, group: int = ECHO_GROUP) -> int:
     return load_library().echo_params_bytes(seg_len, group)
+
+
+def echo_state_bytes(n: int, state_dtype: int) -> int:
+    return load_library().echo_state_bytes(n, state_dtype)
 
 
 def alloc_payload(seg_len: int, bits: int, device, fill: int | None = None) -> Payload:
@@ -143,25 +150,26 @@ def _check(rc: int, where: str):
         raise EchoError(rc, where)
 
 
-def echo_state_reset(cfg: echo_config, S: torch.Tensor, L: torch.Tensor, n: int, stream=None):
-    _check(load_library().echo_state_reset(ctypes.byref(cfg), _ptr(S), _ptr(L), n,
-                                           _stream(stream)), "echo_state_reset")
+def echo_state_reset(cfg: echo_config, state: torch.Tensor, n: int, stream=None):
+    """state: 2n elements (S_j, L_j pairs) of the config's state type."""
+    _check(load_library().echo_state_reset(ctypes.byref(cfg), _ptr(state), n, _stream(stream)),
+           "echo_state_reset")
 
 
 def echo_quantize_feedback(cfg: echo_config, P: int, rank: int, n: int, x: torch.Tensor,
-                           S: torch.Tensor, L: torch.Tensor, out, stream=None):
+                           state: torch.Tensor, out, stream=None):
     """out: list of P Payloads (entry `rank` may be None)."""
-    _check(load_library().echo_quantize_feedback(ctypes.byref(cfg), P, rank, n, _ptr(x), _ptr(S),
-                                                 _ptr(L), _seg_table(P, out), _stream(stream)),
+    _check(load_library().echo_quantize_feedback(ctypes.byref(cfg), P, rank, n, _ptr(x),
+                                                 _ptr(state), _seg_table(P, out), _stream(stream)),
            "echo_quantize_feedback")
 
 
 def echo_owner_reduce_requant(cfg: echo_config, P: int, rank: int, n: int, x: torch.Tensor,
-                              S: torch.Tensor, L: torch.Tensor, inp, out: Payload, stream=None):
+                              state: torch.Tensor, inp, out: Payload, stream=None):
     """inp: list of P Payloads received for segment `rank` (entry `rank` may be None)."""
     out_seg = out.seg()
     _check(load_library().echo_owner_reduce_requant(ctypes.byref(cfg), P, rank, n, _ptr(x),
-                                                    _ptr(S), _ptr(L), _seg_table(P, inp),
+                                                    _ptr(state), _seg_table(P, inp),
                                                     ctypes.byref(out_seg), _stream(stream)),
            "echo_owner_reduce_requant")
 

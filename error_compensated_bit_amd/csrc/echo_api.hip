@@ -84,25 +84,22 @@ int launched() {
 
 extern "C" {
 
-int echo_state_reset(const echo_config* cfg, void* S, void* L, int64_t n, void* stream) {
+int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* stream) {
   if (!cfg) return ECHO_ERR_ARG;
   if (cfg->state_dtype != ECHO_STATE_F32 && cfg->state_dtype != ECHO_STATE_BF16) return ECHO_ERR_ARG;
   if (n <= 0) return ECHO_ERR_ARG;
   int rc;
-  if ((rc = check_buf(S)) || (rc = check_buf(L))) return rc;
-  const uint64_t bytes = (uint64_t)n * (cfg->state_dtype == ECHO_STATE_F32 ? 4u : 2u);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  echo::run_zero(S, bytes, st);
-  echo::run_zero(L, bytes, st);
+  if ((rc = check_buf(state))) return rc;
+  echo::run_zero(state, echo_state_bytes(n, cfg->state_dtype), static_cast<hipStream_t>(stream));
   return launched();
 }
 
 int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n, const void* x,
-                           void* S, void* L, const echo_seg* out, void* stream) {
+                           void* state, const echo_seg* out, void* stream) {
   int rc;
   if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
   if (rank < 0 || rank >= P) return ECHO_ERR_ARG;
-  if ((rc = check_buf(x)) || (rc = check_buf(S)) || (rc = check_buf(L))) return rc;
+  if ((rc = check_buf(x)) || (rc = check_buf(state))) return rc;
   if (!out) return ECHO_ERR_ARG;
   LaunchArgs a = base_args(cfg, P, rank, n);
   for (int p = 0; p < P; ++p) {
@@ -113,19 +110,18 @@ int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n, c
   }
   if (P == 1) return ECHO_OK;  // nothing is sent when a rank owns the whole message
   a.x = x;
-  a.S = S;
-  a.L = L;
+  a.state = state;
   echo::run_quant_feedback(a, static_cast<hipStream_t>(stream));
   return launched();
 }
 
 int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n, const void* x,
-                              void* S, void* L, const echo_seg* in, const echo_seg* out,
+                              void* state, const echo_seg* in, const echo_seg* out,
                               void* stream) {
   int rc;
   if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
   if (rank < 0 || rank >= P) return ECHO_ERR_ARG;
-  if ((rc = check_buf(x)) || (rc = check_buf(S)) || (rc = check_buf(L))) return rc;
+  if ((rc = check_buf(x)) || (rc = check_buf(state))) return rc;
   if (!in && P > 1) return ECHO_ERR_ARG;
   if ((rc = check_seg(out))) return rc;
   LaunchArgs a = base_args(cfg, P, rank, n);
@@ -136,8 +132,7 @@ int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n
     a.segs.params[p] = in[p].params;
   }
   a.x = x;
-  a.S = S;
-  a.L = L;
+  a.state = state;
   a.out_codes = out->codes;
   a.out_params = out->params;
   echo::run_owner_reduce_requant(a, static_cast<hipStream_t>(stream));
@@ -165,6 +160,13 @@ size_t echo_codes_bytes(int64_t seg_len, int bits) {
   if (seg_len <= 0 || (bits != 4 && bits != 8)) return 0;
   if (bits == 4 && seg_len % 2) return 0;
   return (size_t)seg_len * (size_t)bits / 8;
+}
+
+size_t echo_state_bytes(int64_t n, int state_dtype) {
+  if (n <= 0) return 0;
+  if (state_dtype == ECHO_STATE_F32) return (size_t)n * 8;
+  if (state_dtype == ECHO_STATE_BF16) return (size_t)n * 4;
+  return 0;
 }
 
 size_t echo_params_bytes(int64_t seg_len, int group) {

@@ -35,8 +35,7 @@ struct LaunchArgs {
   int P, rank;
   uint64_t seg_len;
   const void* x;
-  void* S;
-  void* L;
+  void* state;   // interleaved short/long memories: state[2j] = S_j, state[2j+1] = L_j
   SegTable segs;
   void* out_codes;
   uint32_t* out_params;

@@ -12,11 +12,20 @@
 // is no dense contraction, so no MFMA; what matters is full-width coalesced
 // loads/stores and keeping every group's min/max reduction inside registers.
 //
-// Thread mapping shared by the entry pass and the owner pass: one group of
-// 128 elements per half-wave (32 lanes), 4 consecutive elements per lane.
-// A wave-wide dwordx4 state access is then 1 KiB contiguous, the 16-bit
-// input a contiguous 512 B dwordx2, and the group min/max a 5-step
-// butterfly of DPP moves plus one ds_swizzle, all within the half-wave.
+// Error-state layout: one array per rank holding the two memories of each
+// element side by side, state[2j] = S_j (short), state[2j+1] = L_j (long).
+// One dwordx4 then carries both memories of 2 elements (fp32 state) or 4
+// elements (bf16 state), so the state is a single contiguous stream; on
+// gfx950 this streams markedly faster than two separate S and L arrays.
+//
+// Thread mapping of the entry and owner passes: EPL consecutive elements per
+// lane (2 for fp32 state, 4 for bf16 state), so a group of 128 elements is
+// one wave (fp32) or one half-wave (bf16), and every wave-wide load or store
+// of the state is 1 KiB contiguous.  The group min/max is a butterfly of DPP
+// moves and a ds_swizzle inside each 32-lane half, plus, for a whole-wave
+// group, a readlane of lanes 0 and 32.  Streamed arrays use nontemporal
+// loads and stores.  One group per wave (or half-wave) per launch slot, with
+// enough blocks to cover the segment: short-lived waves stream best here.
 //
 // Arithmetic is IEEE binary32 with no contraction (the library is built with
 // -ffp-contract=off); the only fused multiply-add is the dequantizer's
@@ -25,6 +34,8 @@
 // of the inputs.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "echo_internal.h"
 
@@ -64,7 +75,8 @@ __device__ __forceinline__ float swz_xor16(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
 
-// Min and max over the 32 lanes of a half-wave; every lane gets the result.
+// Min and max over each 32-lane half of a wave; every lane of a half gets
+// its half's result.
 __device__ __forceinline__ void halfwave_minmax(float& mn, float& mx) {
   mn = fminf(mn, dpp<kDppXor1>(mn));
   mx = fmaxf(mx, dpp<kDppXor1>(mx));
@@ -76,6 +88,27 @@ __device__ __forceinline__ void halfwave_minmax(float& mn, float& mx) {
   mx = fmaxf(mx, dpp<kDppMirror>(mx));
   mn = fminf(mn, swz_xor16(mn));
   mx = fmaxf(mx, swz_xor16(mx));
+}
+
+// Combine the two already-reduced 32-lane halves of a wave (wave-uniform).
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Plain or nontemporal access to streamed arrays.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
 }
 
 // Group parameters of the zero-point-aware asymmetric quantizer ([JP-1]):
@@ -113,60 +146,77 @@ __device__ __forceinline__ float decode(uint32_t code, float sf, float zf) {
   return fmaf((float)code, sf, zf);
 }
 
-// 4 consecutive 16-bit inputs
-template <int IN_T>
-__device__ __forceinline__ void load_in4(const uint16_t* __restrict__ p, float (&v)[4]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  v[0] = in_to_f32<IN_T>(w.x & 0xffffu);
-  v[1] = in_to_f32<IN_T>(w.x >> 16);
-  v[2] = in_to_f32<IN_T>(w.y & 0xffffu);
-  v[3] = in_to_f32<IN_T>(w.y >> 16);
+// EPL consecutive 16-bit inputs (EPL = 2 or 4)
+template <int IN_T, int EPL, bool NT>
+__device__ __forceinline__ void load_in(const uint16_t* __restrict__ p, float* v) {
+  if constexpr (EPL == 2) {
+    const uint32_t w = ld<NT>(reinterpret_cast<const uint32_t*>(p));
+    v[0] = in_to_f32<IN_T>(w & 0xffffu);
+    v[1] = in_to_f32<IN_T>(w >> 16);
+  } else {
+    const u32x2 w = ld<NT>(reinterpret_cast<const u32x2*>(p));
+    v[0] = in_to_f32<IN_T>(w.x & 0xffffu);
+    v[1] = in_to_f32<IN_T>(w.x >> 16);
+    v[2] = in_to_f32<IN_T>(w.y & 0xffffu);
+    v[3] = in_to_f32<IN_T>(w.y >> 16);
+  }
 }
 
-// 4 consecutive state values
+// Both memories of EPL consecutive elements: one 16-byte access.
+// fp32 state: EPL = 2, {S0, L0, S1, L1}; bf16 state: EPL = 4, word i = S_i | L_i << 16.
 template <int ST_T>
-__device__ __forceinline__ void load_state4(const void* base, uint64_t e, float (&v)[4]) {
-  if constexpr (ST_T == kStateF32) {
-    const float4 w = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + e);
-    v[0] = w.x; v[1] = w.y; v[2] = w.z; v[3] = w.w;
-  } else {
-    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + e);
-    v[0] = bf16_to_f32(w.x & 0xffffu);
-    v[1] = bf16_to_f32(w.x >> 16);
-    v[2] = bf16_to_f32(w.y & 0xffffu);
-    v[3] = bf16_to_f32(w.y >> 16);
+struct StateIO {
+  static constexpr int kEPL = (ST_T == kStateF32) ? 2 : 4;
+  template <bool NT>
+  static __device__ __forceinline__ void load(const void* base, uint64_t e, float* s, float* l) {
+    if constexpr (ST_T == kStateF32) {
+      const f32x4 w = ld<NT>(reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + 2 * e));
+      s[0] = w.x; l[0] = w.y; s[1] = w.z; l[1] = w.w;
+    } else {
+      const u32x4 w = ld<NT>(reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + 2 * e));
+      const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = bf16_to_f32(a[i] & 0xffffu);
+        l[i] = bf16_to_f32(a[i] >> 16);
+      }
+    }
   }
-}
-
-template <int ST_T>
-__device__ __forceinline__ void store_state4(void* base, uint64_t e, const float (&v)[4]) {
-  if constexpr (ST_T == kStateF32) {
-    *reinterpret_cast<float4*>(static_cast<float*>(base) + e) = make_float4(v[0], v[1], v[2], v[3]);
-  } else {
-    uint2 w;
-    w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-    w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + e) = w;
+  template <bool NT>
+  static __device__ __forceinline__ void store(void* base, uint64_t e, const float* s, const float* l) {
+    if constexpr (ST_T == kStateF32) {
+      f32x4 w = {s[0], l[0], s[1], l[1]};
+      st<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(base) + 2 * e), w);
+    } else {
+      u32x4 w;
+      w.x = f32_to_bf16(s[0]) | (f32_to_bf16(l[0]) << 16);
+      w.y = f32_to_bf16(s[1]) | (f32_to_bf16(l[1]) << 16);
+      w.z = f32_to_bf16(s[2]) | (f32_to_bf16(l[2]) << 16);
+      w.w = f32_to_bf16(s[3]) | (f32_to_bf16(l[3]) << 16);
+      st<NT>(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + 2 * e), w);
+    }
   }
-}
+};
 
-// Codes of 4 consecutive elements starting at segment index k (k % 4 == 0).
-template <int BITS>
-__device__ __forceinline__ void store_codes4(uint8_t* __restrict__ codes, uint64_t k,
-                                             const uint32_t (&q)[4]) {
-  if constexpr (BITS == 4) {
-    *reinterpret_cast<uint16_t*>(codes + k / 2) =
-        (uint16_t)(q[0] | (q[1] << 4) | (q[2] << 8) | (q[3] << 12));
-  } else {
-    *reinterpret_cast<uint32_t*>(codes + k) = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+// Codes of EPL consecutive elements starting at segment index k (k % EPL == 0):
+// EPL*BITS bits, i.e. 1, 2 or 4 bytes.
+template <int BITS, int EPL>
+struct CodeIO {
+  static constexpr int kBits = BITS * EPL;
+  using word = typename std::conditional<kBits == 8, uint8_t,
+               typename std::conditional<kBits == 16, uint16_t, uint32_t>::type>::type;
+  template <bool NT>
+  static __device__ __forceinline__ void store(uint8_t* __restrict__ codes, uint64_t k, const uint32_t* q) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) w |= q[i] << (BITS * i);
+    st<NT>(reinterpret_cast<word*>(codes + k * BITS / 8), (word)w);
   }
-}
-
-template <int BITS>
-__device__ __forceinline__ uint32_t load_codes4(const uint8_t* __restrict__ codes, uint64_t k) {
-  if constexpr (BITS == 4) return *reinterpret_cast<const uint16_t*>(codes + k / 2);
-  else return *reinterpret_cast<const uint32_t*>(codes + k);
-}
+  template <bool NT>
+  static __device__ __forceinline__ uint32_t load(const uint8_t* __restrict__ codes, uint64_t k) {
+    return ld<NT>(reinterpret_cast<const word*>(codes + k * BITS / 8));
+  }
+};
 
 template <int BITS>
 __device__ __forceinline__ uint32_t code_at(uint32_t word, int i) {
@@ -189,45 +239,65 @@ __device__ __forceinline__ float feedback(float x, float s, float l, float eta) 
 }
 
 constexpr int kThreads = 256;
-constexpr int kHalfWaves = kThreads / 32;
+
+// Mapping of one 128-group onto lanes for a state type (see the file header).
+template <int ST_T>
+struct GroupMap {
+  static constexpr int kEPL = StateIO<ST_T>::kEPL;       // elements per lane
+  static constexpr int kLanes = kGroup / kEPL;            // lanes per group: 64 or 32
+  static constexpr int kGroupsPerBlock = kThreads / kLanes;
+};
+
+// Min and max of a group held by GroupMap<ST_T>::kLanes lanes; every lane gets them.
+template <int ST_T>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
+  halfwave_minmax(mn, mx);
+  if constexpr (GroupMap<ST_T>::kLanes == 64) {
+    mn = fminf(lane_value(mn, 0), lane_value(mn, 32));
+    mx = fmaxf(lane_value(mx, 0), lane_value(mx, 32));
+  }
+}
 
 // ------------------------------------------------------------------ K1
 // Entry pass of `rank` ([JP-1]: only the segments this rank does not own are
 // quantized; [JP-2]: feedback-add, residual and state update fused here).
-// grid.y = P-1 non-owned segments, grid.x strides over the segment's groups.
-template <int BITS, int IN_T, int ST_T>
+// grid.y = P-1 non-owned segments, grid.x covers the segment's groups.
+template <int BITS, int IN_T, int ST_T, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_feedback(
-    const uint16_t* __restrict__ x, void* __restrict__ S, void* __restrict__ L, SegTable out,
-    int rank, uint32_t groups, uint64_t seg_len, Coef c) {
+    const uint16_t* __restrict__ x, void* __restrict__ state, SegTable out, int rank,
+    uint32_t groups, uint64_t seg_len, Coef c) {
+  using M = GroupMap<ST_T>;
+  constexpr int E = M::kEPL;
   const int slot = blockIdx.y;
   const int p = slot + (slot >= rank ? 1 : 0);
   const uint64_t base = (uint64_t)p * seg_len;
   uint8_t* __restrict__ codes = static_cast<uint8_t*>(out.codes[p]);
   uint32_t* __restrict__ params = out.params[p];
-  const uint32_t hw = threadIdx.x >> 5, lane = threadIdx.x & 31;
-  for (uint32_t g = blockIdx.x * kHalfWaves + hw; g < groups; g += gridDim.x * kHalfWaves) {
-    const uint64_t k = (uint64_t)g * kGroup + lane * 4;  // index within the segment
+  const uint32_t gl = threadIdx.x / M::kLanes, lane = threadIdx.x % M::kLanes;
+  for (uint32_t g = blockIdx.x * M::kGroupsPerBlock + gl; g < groups;
+       g += gridDim.x * M::kGroupsPerBlock) {
+    const uint64_t k = (uint64_t)g * kGroup + lane * E;   // index within the segment
     const uint64_t e = base + k;
-    float xv[4], s[4], l[4], v[4];
-    load_in4<IN_T>(x + e, xv);
-    load_state4<ST_T>(S, e, s);
-    load_state4<ST_T>(L, e, l);
+    float xv[E], s[E], l[E], v[E];
+    load_in<IN_T, E, NT>(x + e, xv);
+    StateIO<ST_T>::template load<NT>(state, e, s, l);
+    float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = feedback(xv[i], s[i], l[i], c.eta);
-    float mn = fminf(fminf(v[0], v[1]), fminf(v[2], v[3]));
-    float mx = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-    halfwave_minmax(mn, mx);
-    const QParams qp = group_params<BITS>(mn, mx);
-    uint32_t q[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      q[i] = encode<BITS>(v[i], qp);
-      const float r = v[i] - decode(q[i], qp.sf, qp.zf);
-      ema(s[i], l[i], r, c);
+    for (int i = 0; i < E; ++i) {
+      v[i] = feedback(xv[i], s[i], l[i], c.eta);
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
     }
-    store_state4<ST_T>(S, e, s);
-    store_state4<ST_T>(L, e, l);
-    store_codes4<BITS>(codes, k, q);
+    group_minmax<ST_T>(mn, mx);
+    const QParams qp = group_params<BITS>(mn, mx);
+    uint32_t q[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      q[i] = encode<BITS>(v[i], qp);
+      ema(s[i], l[i], v[i] - decode(q[i], qp.sf, qp.zf), c);
+    }
+    StateIO<ST_T>::template store<NT>(state, e, s, l);
+    CodeIO<BITS, E>::template store<NT>(codes, k, q);
     if (lane == 0) params[g] = qp.word;
   }
 }
@@ -236,63 +306,68 @@ __global__ __launch_bounds__(kThreads) void k_quant_feedback(
 // Owner pass over segment `rank` ([JP-1]: sum in fp32 in rank order with the
 // owner's own unquantized term, requantize; [JP-W] the round trip; [JP-2]
 // the owner's residual against the output value, state update fused).
-template <int BITS, int IN_T, int ST_T, int OUT_T>
+template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT>
 __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
-    const uint16_t* __restrict__ x, void* __restrict__ S, void* __restrict__ L, SegTable in,
-    int P, int rank, uint32_t groups, uint64_t seg_len, uint8_t* __restrict__ out_codes,
+    const uint16_t* __restrict__ x, void* __restrict__ state, SegTable in, int P, int rank,
+    uint32_t groups, uint64_t seg_len, uint8_t* __restrict__ out_codes,
     uint32_t* __restrict__ out_params, Coef c) {
+  using M = GroupMap<ST_T>;
+  constexpr int E = M::kEPL;
   const uint64_t base = (uint64_t)rank * seg_len;
-  const uint32_t hw = threadIdx.x >> 5, lane = threadIdx.x & 31;
-  for (uint32_t g = blockIdx.x * kHalfWaves + hw; g < groups; g += gridDim.x * kHalfWaves) {
-    const uint64_t k = (uint64_t)g * kGroup + lane * 4;
+  const uint32_t gl = threadIdx.x / M::kLanes, lane = threadIdx.x % M::kLanes;
+  for (uint32_t g = blockIdx.x * M::kGroupsPerBlock + gl; g < groups;
+       g += gridDim.x * M::kGroupsPerBlock) {
+    const uint64_t k = (uint64_t)g * kGroup + lane * E;
     const uint64_t e = base + k;
     // incoming payload words first, so that all loads are in flight together
     uint32_t cw[kMaxRanks], pw[kMaxRanks];
 #pragma unroll
     for (int p = 0; p < kMaxRanks; ++p) {
       if (p < P && p != rank) {
-        cw[p] = load_codes4<BITS>(static_cast<const uint8_t*>(in.codes[p]), k);
+        cw[p] = CodeIO<BITS, E>::template load<NT>(static_cast<const uint8_t*>(in.codes[p]), k);
         pw[p] = in.params[p][g];
       }
     }
-    float xv[4], s[4], l[4], own[4];
-    load_in4<IN_T>(x + e, xv);
-    load_state4<ST_T>(S, e, s);
-    load_state4<ST_T>(L, e, l);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) own[i] = feedback(xv[i], s[i], l[i], c.eta);
-    float acc[4];
+    float xv[E], s[E], l[E], acc[E];
+    load_in<IN_T, E, NT>(x + e, xv);
+    StateIO<ST_T>::template load<NT>(state, e, s, l);
 #pragma unroll
     for (int p = 0; p < kMaxRanks; ++p) {
       if (p < P) {
-        float t[4];
         if (p == rank) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t[i] = own[i];
+          for (int i = 0; i < E; ++i) {
+            const float t = feedback(xv[i], s[i], l[i], c.eta);
+            acc[i] = (p == 0) ? t : acc[i] + t;
+          }
         } else {
           const float sf = f16_to_f32(pw[p] & 0xffffu), zf = f16_to_f32(pw[p] >> 16);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) t[i] = decode(code_at<BITS>(cw[p], i), sf, zf);
+          for (int i = 0; i < E; ++i) {
+            const float t = decode(code_at<BITS>(cw[p], i), sf, zf);
+            acc[i] = (p == 0) ? t : acc[i] + t;
+          }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = (p == 0) ? t[i] : acc[i] + t[i];
       }
     }
-    float mn = fminf(fminf(acc[0], acc[1]), fminf(acc[2], acc[3]));
-    float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-    halfwave_minmax(mn, mx);
-    const QParams qp = group_params<BITS>(mn, mx);
-    uint32_t q[4];
+    float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < E; ++i) {
+      mn = fminf(mn, acc[i]);
+      mx = fmaxf(mx, acc[i]);
+    }
+    group_minmax<ST_T>(mn, mx);
+    const QParams qp = group_params<BITS>(mn, mx);
+    uint32_t q[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
       q[i] = encode<BITS>(acc[i], qp);
       const float d = decode(q[i], qp.sf, qp.zf);
       const float o = (OUT_T == kOutBF16) ? bf16_to_f32(f32_to_bf16(d)) : d;
       ema(s[i], l[i], acc[i] - o, c);
     }
-    store_state4<ST_T>(S, e, s);
-    store_state4<ST_T>(L, e, l);
-    store_codes4<BITS>(out_codes, k, q);
+    StateIO<ST_T>::template store<NT>(state, e, s, l);
+    CodeIO<BITS, E>::template store<NT>(out_codes, k, q);
     if (lane == 0) out_params[g] = qp.word;
   }
 }
@@ -301,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
 // Dequantize the P owners' payloads into the output ([JP-1]).
 // bf16 output: 8 elements per lane (one 16-byte store), 16 lanes per group;
 // fp32 output: 4 elements per lane (one 16-byte store), 32 lanes per group.
-template <int BITS, int OUT_T>
+template <int BITS, int OUT_T, bool NT>
 __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32_t groups,
                                                              uint64_t seg_len, void* __restrict__ out) {
   constexpr int EPL = (OUT_T == kOutBF16) ? 8 : 4;
@@ -318,35 +393,35 @@ __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32
     const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
     float d[EPL];
     if constexpr (BITS == 4 && EPL == 8) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + k / 2);
+      const uint32_t w = ld<NT>(reinterpret_cast<const uint32_t*>(codes + k / 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) d[i] = decode((w >> (4 * i)) & 0xfu, sf, zf);
     } else if constexpr (BITS == 4) {
-      const uint32_t w = *reinterpret_cast<const uint16_t*>(codes + k / 2);
+      const uint32_t w = ld<NT>(reinterpret_cast<const uint16_t*>(codes + k / 2));
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = decode((w >> (4 * i)) & 0xfu, sf, zf);
     } else if constexpr (EPL == 8) {
-      const uint2 w = *reinterpret_cast<const uint2*>(codes + k);
+      const u32x2 w = ld<NT>(reinterpret_cast<const u32x2*>(codes + k));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         d[i] = decode((w.x >> (8 * i)) & 0xffu, sf, zf);
         d[4 + i] = decode((w.y >> (8 * i)) & 0xffu, sf, zf);
       }
     } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + k);
+      const uint32_t w = ld<NT>(reinterpret_cast<const uint32_t*>(codes + k));
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = decode((w >> (8 * i)) & 0xffu, sf, zf);
     }
     if constexpr (OUT_T == kOutBF16) {
-      uint4 o;
+      u32x4 o;
       o.x = f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16);
       o.y = f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16);
       o.z = f32_to_bf16(d[4]) | (f32_to_bf16(d[5]) << 16);
       o.w = f32_to_bf16(d[6]) | (f32_to_bf16(d[7]) << 16);
-      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + base + k) = o;
+      st<NT>(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + base + k), o);
     } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(out) + base + k) =
-          make_float4(d[0], d[1], d[2], d[3]);
+      f32x4 o = {d[0], d[1], d[2], d[3]};
+      st<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(out) + base + k), o);
     }
   }
 }
@@ -366,9 +441,10 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint8_t* __restrict__ a, uint
 // ------------------------------------------------------------------ launchers
 namespace {
 
-// Blocks along x: enough for one group per half-wave, capped so very large
-// segments stride (each block then handles several groups).
-unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned ny) {
+// Blocks along x: `grid_x` when given, else enough for one group per lane
+// run (capped, so very large segments stride).
+unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned ny, unsigned grid_x) {
+  if (grid_x) return grid_x;
   const uint64_t want = (groups + groups_per_block - 1) / groups_per_block;
   const uint64_t cap = (kGridCap + ny - 1) / ny;
   const uint64_t b = want < cap ? want : cap;
@@ -377,40 +453,43 @@ unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned ny) {
 
 }  // namespace
 
-template <int BITS, int IN_T, int ST_T>
-static void launch_k1(const LaunchArgs& a, hipStream_t st) {
+template <int BITS, int IN_T, int ST_T, bool NT>
+void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
   const unsigned ny = (unsigned)(a.P - 1);
-  dim3 grid(blocks_for(groups, kHalfWaves, ny), ny);
-  hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T>), grid, dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(a.x), a.S, a.L, a.segs, a.rank,
+  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, ny, grid_x), ny);
+  hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, NT>), grid, dim3(kThreads), 0, st,
+                     static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
                      (uint32_t)groups, a.seg_len, a.coef);
 }
 
-template <int BITS, int IN_T, int ST_T, int OUT_T>
-static void launch_k2(const LaunchArgs& a, hipStream_t st) {
+template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT>
+void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
-  dim3 grid(blocks_for(groups, kHalfWaves, 1));
-  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T>), grid, dim3(kThreads), 0,
-                     st, static_cast<const uint16_t*>(a.x), a.S, a.L, a.segs, a.P, a.rank,
-                     (uint32_t)groups, a.seg_len, static_cast<uint8_t*>(a.out_codes),
-                     a.out_params, a.coef);
+  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, 1, grid_x));
+  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, NT>), grid,
+                     dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, a.segs,
+                     a.P, a.rank, (uint32_t)groups, a.seg_len,
+                     static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
 }
 
-template <int BITS, int OUT_T>
-static void launch_k3(const LaunchArgs& a, hipStream_t st) {
+template <int BITS, int OUT_T, bool NT>
+void launch_k3(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
   constexpr int gpb = kThreads / (kGroup / ((OUT_T == kOutBF16) ? 8 : 4));
   const unsigned ny = (unsigned)a.P;
-  dim3 grid(blocks_for(groups, gpb, ny), ny);
-  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T>), grid, dim3(kThreads), 0, st, a.segs,
+  dim3 grid(blocks_for(groups, gpb, ny, grid_x), ny);
+  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, NT>), grid, dim3(kThreads), 0, st, a.segs,
                      (uint32_t)groups, a.seg_len, a.out);
 }
+
+// Nontemporal loads and stores for every streamed array.
+constexpr bool kNT = true;
 
 // Runtime -> template dispatch.
 void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
 #define ECHO_K1(B, I, S) \
-  if (a.bits == B && a.in_dtype == I && a.state_dtype == S) return launch_k1<B, I, S>(a, st);
+  if (a.bits == B && a.in_dtype == I && a.state_dtype == S) return launch_k1<B, I, S, kNT>(a, 0, st);
   ECHO_K1(4, kInBF16, kStateF32) ECHO_K1(4, kInBF16, kStateBF16)
   ECHO_K1(4, kInF16, kStateF32)  ECHO_K1(4, kInF16, kStateBF16)
   ECHO_K1(8, kInBF16, kStateF32) ECHO_K1(8, kInBF16, kStateBF16)
@@ -419,9 +498,9 @@ void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
 }
 
 void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
-#define ECHO_K2(B, I, S, O)                                                             \
+#define ECHO_K2(B, I, S, O)                                                      \
   if (a.bits == B && a.in_dtype == I && a.state_dtype == S && a.out_dtype == O) \
-    return launch_k2<B, I, S, O>(a, st);
+    return launch_k2<B, I, S, O, kNT>(a, 0, st);
 #define ECHO_K2_IO(B, I) \
   ECHO_K2(B, I, kStateF32, kOutBF16) ECHO_K2(B, I, kStateF32, kOutF32) \
   ECHO_K2(B, I, kStateBF16, kOutBF16) ECHO_K2(B, I, kStateBF16, kOutF32)
@@ -431,10 +510,10 @@ void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
 }
 
 void run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
-  if (a.bits == 4 && a.out_dtype == kOutBF16) return launch_k3<4, kOutBF16>(a, st);
-  if (a.bits == 4 && a.out_dtype == kOutF32) return launch_k3<4, kOutF32>(a, st);
-  if (a.bits == 8 && a.out_dtype == kOutBF16) return launch_k3<8, kOutBF16>(a, st);
-  if (a.bits == 8 && a.out_dtype == kOutF32) return launch_k3<8, kOutF32>(a, st);
+  if (a.bits == 4 && a.out_dtype == kOutBF16) return launch_k3<4, kOutBF16, kNT>(a, 0, st);
+  if (a.bits == 4 && a.out_dtype == kOutF32) return launch_k3<4, kOutF32, kNT>(a, 0, st);
+  if (a.bits == 8 && a.out_dtype == kOutBF16) return launch_k3<8, kOutBF16, kNT>(a, 0, st);
+  if (a.bits == 8 && a.out_dtype == kOutF32) return launch_k3<8, kOutF32, kNT>(a, 0, st);
 }
 
 void run_zero(void* p, uint64_t bytes, hipStream_t st) {

@@ -24,11 +24,11 @@ def out_torch_dtype(cfg: B.echo_config) -> torch.dtype:
 
 @dataclass
 class Ranks:
-    """Error state and payload buffers of P ranks with n-element messages."""
+    """Error state and payload buffers of P ranks with n-element messages.
+    state[p] holds rank p's short and long memories side by side (2n elements)."""
     P: int
     n: int
-    S: list
-    L: list
+    state: list
     sent: list      # sent[p][o]: payload rank p sends to owner o (None for o == p)
     owned: list     # owned[o]: owner o's requantized payload
     out: torch.Tensor
@@ -44,25 +44,24 @@ def alloc_ranks(cfg: B.echo_config, P: int, n: int, device, bits_max: int | None
     bits = bits_max or cfg.bits
     seg = n // P
     sdt = state_torch_dtype(cfg)
-    S = [torch.empty(n, dtype=sdt, device=device) for _ in range(P)]
-    L = [torch.empty(n, dtype=sdt, device=device) for _ in range(P)]
+    state = [torch.empty(2 * n, dtype=sdt, device=device) for _ in range(P)]
     sent = [[None if o == p else B.alloc_payload(seg, bits, device) for o in range(P)]
             for p in range(P)]
     owned = [B.alloc_payload(seg, bits, device) for _ in range(P)]
     out = torch.empty(n, dtype=out_torch_dtype(cfg), device=device)
-    r = Ranks(P, n, S, L, sent, owned, out)
+    r = Ranks(P, n, state, sent, owned, out)
     for p in range(P):
-        B.echo_state_reset(cfg, S[p], L[p], n)
+        B.echo_state_reset(cfg, state[p], n)
     return r
 
 
 def entry(cfg, r: Ranks, p: int, x: torch.Tensor, stream=None):
-    B.echo_quantize_feedback(cfg, r.P, p, r.n, x, r.S[p], r.L[p], r.sent[p], stream)
+    B.echo_quantize_feedback(cfg, r.P, p, r.n, x, r.state[p], r.sent[p], stream)
 
 
 def owner(cfg, r: Ranks, o: int, x: torch.Tensor, stream=None):
     inp = [None if p == o else r.sent[p][o] for p in range(r.P)]
-    B.echo_owner_reduce_requant(cfg, r.P, o, r.n, x, r.S[o], r.L[o], inp, r.owned[o], stream)
+    B.echo_owner_reduce_requant(cfg, r.P, o, r.n, x, r.state[o], inp, r.owned[o], stream)
 
 
 def gather(cfg, r: Ranks, stream=None):

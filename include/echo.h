@@ -30,8 +30,11 @@
  *     bits = 8 -> one per byte.  Codes and params of a segment are two
  *     separate arrays ("payload", echo_seg).
  *   - Dequantized value = fma(code, scale, zero) in fp32.
- *   - Error state: two arrays S (short memory) and L (long memory) of n
- *     elements per rank, fp32 or bf16 (config), updated in place.
+ *   - Error state: one array per rank of 2n elements of the config's
+ *     state type (fp32 or bf16) holding the short memory S and the long
+ *     memory L of each element side by side: state[2j] = S_j,
+ *     state[2j+1] = L_j.  It is updated in place and persists between
+ *     calls (checkpointing it = copying it).
  *
  * Conventions:
  *   - All buffer pointers are device pointers, 16-byte aligned; the caller
@@ -41,7 +44,7 @@
  *     buffers may run concurrently.
  *   - All calls are asynchronous on `stream` (a hipStream_t; NULL = the
  *     default stream) and never synchronize.
- *   - Payload buffers must not overlap x, S, L, the output or each other.
+ *   - Payload buffers must not overlap x, the state, the output or each other.
  *   - Every call validates all arguments before touching the GPU and
  *     returns ECHO_OK or a negative error code; nothing is launched when an
  *     error is returned.  No exception crosses this interface.
@@ -93,53 +96,56 @@ typedef struct echo_seg {
 } echo_seg;
 
 /*
- * echo_state_reset -- empty both memories: S[j] = L[j] = +0 for j < n.
- *   S, L: device arrays of n elements of the config's state type.
+ * echo_state_reset -- empty both memories: S_j = L_j = +0 for j < n.
+ *   state: device array of echo_state_bytes(n, cfg->state_dtype) bytes.
  *   The feedback of [JP-2] carries error into later calls; a chain of calls
  *   starts from an empty state.  Implemented as a fill kernel (no memset
  *   node), so it may be captured in a HIP graph.
  *   Errors: ECHO_ERR_ARG (null cfg/pointer, n <= 0, bad state type),
  *   ECHO_ERR_ALIGN, ECHO_ERR_HIP.
  */
-int echo_state_reset(const echo_config* cfg, void* S, void* L, int64_t n, void* stream);
+int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* stream);
 
 /*
  * echo_quantize_feedback -- entry pass of rank `rank` ([JP-1], [JP-2]).
  *   For every element j of every segment p != rank:
- *     v = x[j] + eta * (S[j] + L[j])                 (fp32, unfused)
+ *     v = x[j] + eta * (S_j + L_j)                   (fp32, unfused)
  *   each 128-group of v is quantized to `bits` with an fp16 zero point
  *   (the group minimum) and fp16 step ((max - zero) / (2^bits - 1)), codes
  *   round half to even; the payload goes to out[p].  With r = v - dequant:
- *     S[j] = beta_short * S[j] + (1-beta_short)(1-mix_long) * r
- *     L[j] = beta_long  * L[j] + (1-beta_long) * mix_long   * r
+ *     S_j = beta_short * S_j + (1-beta_short)(1-mix_long) * r
+ *     L_j = beta_long  * L_j + (1-beta_long) * mix_long   * r
+ *   (each product rounded to fp32, then the sum; the two weights are
+ *   computed in double from the float parameters and rounded once).
  *   The owned segment is not read or written (its feedback is applied by
  *   echo_owner_reduce_requant); P = 1 launches nothing.
- *   x: device, n 16-bit elements (in_dtype).  S, L: device, n elements.
+ *   x: device, n 16-bit elements (in_dtype).  state: device, n (S, L) pairs.
  *   out: host array of P echo_seg; out[rank] is ignored, every other entry
  *   must point at a payload sized for n/P elements.
  *   Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_ALIGN, ECHO_ERR_HIP.
  */
 int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n,
-                           const void* x, void* S, void* L,
+                           const void* x, void* state,
                            const echo_seg* out, void* stream);
 
 /*
  * echo_owner_reduce_requant -- owner pass of rank `rank` over its segment
  * ([JP-1]: the owner sums in high precision and requantizes; [JP-W]).
  *   For every element j of segment `rank`:
- *     v_own = x[j] + eta * (S[j] + L[j])
+ *     v_own = x[j] + eta * (S_j + L_j)
  *     acc   = sum over p = 0..P-1 in that order of
  *             (p == rank ? v_own : dequant of in[p]'s code for j)    (fp32)
  *   acc is requantized per 128-group into *out (same quantizer as above);
  *   o = the output value of j (bf16-rounded dequant for ECHO_OUT_BF16,
- *   the fp32 dequant for ECHO_OUT_F32); r = acc - o; S and L are updated
- *   with r as above.  Segments p != rank are not read or written in x, S, L.
+ *   the fp32 dequant for ECHO_OUT_F32); r = acc - o; S_j and L_j are
+ *   updated with r as above.  Segments p != rank of x and state are not
+ *   read or written.
  *   in: host array of P echo_seg (payloads the other ranks sent for this
  *   segment); in[rank] is ignored.  out: host pointer to one echo_seg.
  *   Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_ALIGN, ECHO_ERR_HIP.
  */
 int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n,
-                              const void* x, void* S, void* L,
+                              const void* x, void* state,
                               const echo_seg* in, const echo_seg* out, void* stream);
 
 /*
@@ -153,9 +159,11 @@ int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n
 int echo_dequant_gather(const echo_config* cfg, int P, int64_t n,
                         const echo_seg* in, void* out, void* stream);
 
-/* Payload sizes for a segment of seg_len elements (0 for invalid input). */
+/* Buffer sizes (0 for invalid input): payload of a segment of seg_len
+ * elements, and the error state of an n-element message. */
 size_t echo_codes_bytes(int64_t seg_len, int bits);
 size_t echo_params_bytes(int64_t seg_len, int group);
+size_t echo_state_bytes(int64_t n, int state_dtype);
 
 /* Static description of an error code. */
 const char* echo_error_string(int code);

@@ -93,3 +93,24 @@ def random_payload_host(rng, seg: int, bits: int):
 def to_device_payload(codes: np.ndarray, params: np.ndarray, device) -> B.Payload:
     return B.Payload(torch.from_numpy(codes.copy()).to(device),
                      torch.from_numpy(params.view(np.int32).copy()).to(device))
+
+
+def interleave(S: np.ndarray, L: np.ndarray) -> np.ndarray:
+    """Device state layout from the oracle's two arrays: state[2j] = S_j, state[2j+1] = L_j."""
+    out = np.empty(2 * S.size, S.dtype)
+    out[0::2] = S
+    out[1::2] = L
+    return out
+
+
+def split_state(t: torch.Tensor):
+    """(S, L) host arrays from a device state buffer."""
+    h = host(t)
+    return h[0::2].copy(), h[1::2].copy()
+
+
+def gather_state(t: torch.Tensor, idx: np.ndarray):
+    """(S, L) of the elements `idx` from a device state buffer."""
+    both = np.stack([2 * idx, 2 * idx + 1], axis=1).reshape(-1)
+    h = gather_elems(t, both)
+    return h[0::2].copy(), h[1::2].copy()

@@ -33,6 +33,13 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n), n
 
 
+def test_state_sizes():
+    assert B.echo_state_bytes(1000, B.ECHO_STATE_F32) == 8000
+    assert B.echo_state_bytes(1000, B.ECHO_STATE_BF16) == 4000
+    assert B.echo_state_bytes(0, B.ECHO_STATE_F32) == 0
+    assert B.echo_state_bytes(10, 7) == 0
+
+
 def test_payload_sizes():
     assert B.echo_codes_bytes(1024, 4) == 512
     assert B.echo_codes_bytes(1024, 8) == 1024
@@ -63,43 +70,44 @@ def cfg(**kw):
 
 
 @pytest.mark.parametrize("call,code", [
-    (lambda L: L.echo_quantize_feedback(None, 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(bits=3), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(group=64), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(in_dtype=7), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(eta=float("nan")), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(beta_short=1.0), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(beta_long=-0.1), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(mix_long=1.5), 2, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(), 0, 0, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(), 17, 0, 17 * 128, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, 2, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, -1, 256, A, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 0, A, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 384, A, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, None, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A + 8, A, A, SEGS, None), B.ECHO_ERR_ALIGN),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A, A + 4, SEGS, None), B.ECHO_ERR_ALIGN),
-    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A, A, None, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(None, 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(bits=3), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(group=64), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(in_dtype=7), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(eta=float("nan")), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(beta_short=1.0), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(beta_long=-0.1), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(mix_long=1.5), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 0, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 17, 0, 17 * 128, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 2, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, -1, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 0, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 384, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, None, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A + 8, A, SEGS, None), B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A + 4, SEGS, None), B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A, None, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(
-        cfg(), 2, 0, 256, A, A, A, (B.echo_seg * 2)(B.echo_seg(A, A), B.echo_seg(None, A)), None),
+        cfg(), 2, 0, 256, A, A, (B.echo_seg * 2)(B.echo_seg(A, A), B.echo_seg(None, A)), None),
      B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(
-        cfg(), 2, 0, 256, A, A, A, (B.echo_seg * 2)(B.echo_seg(A, A), B.echo_seg(A, A + 2)), None),
+        cfg(), 2, 0, 256, A, A, (B.echo_seg * 2)(B.echo_seg(A, A), B.echo_seg(A, A + 2)), None),
      B.ECHO_ERR_ALIGN),
-    (lambda L: L.echo_owner_reduce_requant(cfg(), 2, 0, 256, A, A, A, SEGS, None, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_owner_reduce_requant(cfg(), 2, 0, 256, A, A, A, None, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_owner_reduce_requant(cfg(), 4, 1, 4 * 128 * 3 + 128, A, A, A, SEGS, SEGS, None),
+    (lambda L: L.echo_owner_reduce_requant(cfg(), 2, 0, 256, A, A, SEGS, None, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_owner_reduce_requant(cfg(), 2, 0, 256, A, A, None, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_owner_reduce_requant(cfg(), 4, 1, 4 * 128 * 3 + 128, A, A, SEGS, SEGS, None),
      B.ECHO_ERR_SHAPE),
-    (lambda L: L.echo_owner_reduce_requant(cfg(bits=8, out_dtype=2), 2, 0, 256, A, A, A, SEGS, SEGS, None),
+    (lambda L: L.echo_owner_reduce_requant(cfg(bits=8, out_dtype=2), 2, 0, 256, A, A, SEGS, SEGS, None),
      B.ECHO_ERR_ARG),
     (lambda L: L.echo_dequant_gather(cfg(), 2, 256, None, A, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_dequant_gather(cfg(), 2, 256, SEGS, A + 1, None), B.ECHO_ERR_ALIGN),
     (lambda L: L.echo_dequant_gather(cfg(), 2, 200, SEGS, A, None), B.ECHO_ERR_SHAPE),
-    (lambda L: L.echo_state_reset(None, A, A, 10, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_state_reset(cfg(state_dtype=5), A, A, 10, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_state_reset(cfg(), A, A, 0, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_state_reset(cfg(), A, A + 8, 10, None), B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_state_reset(None, A, 10, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_state_reset(cfg(state_dtype=5), A, 10, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_state_reset(cfg(), A, 0, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_state_reset(cfg(), A + 8, 10, None), B.ECHO_ERR_ALIGN),
+    (lambda L: L.echo_state_reset(cfg(), None, 10, None), B.ECHO_ERR_ARG),
 ])
 def test_invalid_arguments_return_codes(call, code):
     assert call(B.load_library()) == code

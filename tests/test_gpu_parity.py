@@ -14,8 +14,8 @@ import oracle as O
 from error_compensated_bit_amd import binding as B
 from error_compensated_bit_amd import sim
 from echo_testutil import (G, assert_bits_equal, assert_float_close, device_bits16, host,
-                           oracle_config, random_payload_host, state_as_f32,
-                           to_device_payload)
+                           interleave, oracle_config, random_payload_host, split_state,
+                           state_as_f32, to_device_payload)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -57,10 +57,16 @@ def state_dev(a):
     return torch.from_numpy(a.copy()).to(DEV)
 
 
-def cmp_state(gpu_t, ref, what):
-    g = host(gpu_t)
+def cmp_arrays(g, ref, what):
     assert_float_close(state_as_f32(g), state_as_f32(ref), what)
     assert_bits_equal(g, ref, what + " (bits)")
+
+
+def cmp_state(gpu_state, S_ref, L_ref, what):
+    """Device state buffer (S_j, L_j pairs) against the oracle's S and L."""
+    S, L = split_state(gpu_state)
+    cmp_arrays(S, S_ref, what + " short memory")
+    cmp_arrays(L, L_ref, what + " long memory")
 
 
 # ------------------------------------------------------------------ entry pass
@@ -78,9 +84,9 @@ def test_entry_pass(P, groups, bits, in_dtype, state_dtype):
         xb, tdt = rand_input(rng, n, in_dtype, special=(rank == 0))
         s0, l0 = rand_state(rng, n, state_dtype), rand_state(rng, n, state_dtype, 0.2)
         x = device_bits16(xb, tdt, DEV)
-        S, L = state_dev(s0), state_dev(l0)
+        state = state_dev(interleave(s0, l0))
         out = [B.alloc_payload(seg, bits, DEV, fill=0xA5) for _ in range(P)]
-        B.echo_quantize_feedback(cfg, P, rank, n, x, S, L, out)
+        B.echo_quantize_feedback(cfg, P, rank, n, x, state, out)
         torch.cuda.synchronize()
         oc = [np.zeros(seg * bits // 8, np.uint8) if p != rank else None for p in range(P)]
         op = [np.zeros(groups, np.uint32) if p != rank else None for p in range(P)]
@@ -93,10 +99,11 @@ def test_entry_pass(P, groups, bits, in_dtype, state_dtype):
                 continue
             assert_bits_equal(host(out[p].codes), oc[p], f"codes p={p}")
             assert_bits_equal(host(out[p].params), op[p], f"params p={p}")
-        cmp_state(S, so, "S")
-        cmp_state(L, lo, "L")
+        cmp_state(state, so, lo, "state")
         own = slice(rank * seg, (rank + 1) * seg)
-        assert_bits_equal(host(S)[own], s0[own], "owned S untouched")
+        S, L = split_state(state)
+        assert_bits_equal(S[own], s0[own], "owned S untouched")
+        assert_bits_equal(L[own], l0[own], "owned L untouched")
 
 
 # ------------------------------------------------------------------ owner pass
@@ -120,10 +127,10 @@ def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype):
             c = k.astype(np.uint8) if bits == 8 else (k[0::2] | (k[1::2] << 4)).astype(np.uint8)
             inc[1] = (c, np.full(groups, 0x3C00, np.uint32))
         x = device_bits16(xb, tdt, DEV)
-        S, L = state_dev(s0), state_dev(l0)
+        state = state_dev(interleave(s0, l0))
         inp = [None if pl is None else to_device_payload(pl[0], pl[1], DEV) for pl in inc]
         out = B.alloc_payload(seg, bits, DEV, fill=0x5A)
-        B.echo_owner_reduce_requant(cfg, P, rank, n, x, S, L, inp, out)
+        B.echo_owner_reduce_requant(cfg, P, rank, n, x, state, inp, out)
         torch.cuda.synchronize()
         oc = np.zeros(seg * bits // 8, np.uint8)
         op = np.zeros(groups, np.uint32)
@@ -133,12 +140,12 @@ def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype):
                                [None if pl is None else pl[1] for pl in inc], oc, op)
         assert_bits_equal(host(out.codes), oc, "owner codes")
         assert_bits_equal(host(out.params), op, "owner params")
-        cmp_state(S, so, "S")
-        cmp_state(L, lo, "L")
+        cmp_state(state, so, lo, "state")
         other = np.ones(n, bool)
         other[rank * seg:(rank + 1) * seg] = False
-        assert_bits_equal(host(S)[other], s0[other], "non-owned S untouched")
-        assert_bits_equal(host(L)[other], l0[other], "non-owned L untouched")
+        S, L = split_state(state)
+        assert_bits_equal(S[other], s0[other], "non-owned S untouched")
+        assert_bits_equal(L[other], l0[other], "non-owned L untouched")
 
 
 # ------------------------------------------------------------------ dequantize
@@ -170,14 +177,13 @@ def test_dequant_gather(P, groups, bits, out_dtype):
 def test_state_reset(n, state_dtype):
     cfg = B.make_config(state_dtype=state_dtype)
     dt = sim.state_torch_dtype(cfg)
-    S = torch.full((n + 16,), -1.5, dtype=dt, device=DEV)
-    L = torch.full((n + 16,), 2.5, dtype=dt, device=DEV)
-    B.echo_state_reset(cfg, S, L, n)
+    state = torch.full((2 * n + 16,), -1.5, dtype=dt, device=DEV)
+    assert B.echo_state_bytes(n, state_dtype) == 2 * n * state.element_size()
+    B.echo_state_reset(cfg, state, n)
     torch.cuda.synchronize()
-    for t in (S, L):
-        h = host(t)[:n]
-        assert not h.view(np.uint32 if h.dtype == np.float32 else np.uint16).any()
-    assert torch.all(S[n:] == -1.5) and torch.all(L[n:] == 2.5)
+    h = host(state)[:2 * n]
+    assert not h.view(np.uint32 if h.dtype == np.float32 else np.uint16).any()
+    assert torch.all(state[2 * n:] == -1.5)
 
 
 # ------------------------------------------------------------------ whole call
@@ -213,8 +219,7 @@ def test_allreduce_three_calls(P, groups, bits, out_dtype, state_dtype):
                     assert_bits_equal(host(r.sent[p][o].params), sent[p][o][1], f"sent params {p}->{o}")
             assert_bits_equal(host(r.owned[p].codes), owned[p][0], f"owned codes {p}")
             assert_bits_equal(host(r.owned[p].params), owned[p][1], f"owned params {p}")
-            cmp_state(r.S[p], oS[p], f"S rank {p} site {site}")
-            cmp_state(r.L[p], oL[p], f"L rank {p} site {site}")
+            cmp_state(r.state[p], oS[p], oL[p], f"rank {p} site {site}")
         got = host(r.out)
         if out_dtype == B.ECHO_OUT_F32:
             assert_float_close(got, out, "output")
@@ -243,13 +248,13 @@ def test_runs_on_the_callers_stream():
 def test_invalid_arguments_raise():
     cfg = B.make_config()
     x = torch.zeros(1024, dtype=torch.bfloat16, device=DEV)
-    S = torch.zeros(1024, device=DEV)
+    state = torch.zeros(2048, device=DEV)
     out = [B.alloc_payload(512, 4, DEV) for _ in range(2)]
     with pytest.raises(B.EchoError) as e:
-        B.echo_quantize_feedback(cfg, 2, 0, 1000, x, S, S, out)
+        B.echo_quantize_feedback(cfg, 2, 0, 1000, x, state, out)
     assert e.value.code == B.ECHO_ERR_SHAPE
     with pytest.raises(B.EchoError) as e:
-        B.echo_quantize_feedback(cfg, 2, 0, 1024, x[1:], S, S, out)
+        B.echo_quantize_feedback(cfg, 2, 0, 1024, x[1:], state, out)
     assert e.value.code == B.ECHO_ERR_ALIGN
     bad = B.make_config(bits=3)
     with pytest.raises(B.EchoError) as e:

@@ -18,7 +18,7 @@ import oracle as O
 from error_compensated_bit_amd import binding as B
 from error_compensated_bit_amd import sim
 from error_compensated_bit_amd.inputs import WORKLOADS, make_x
-from echo_testutil import (G, assert_bits_equal, gather_elems, group_index, host,
+from echo_testutil import (G, assert_bits_equal, gather_elems, gather_state, group_index,
                            oracle_config, payload_groups)
 
 pytestmark = pytest.mark.gpu
@@ -49,8 +49,9 @@ def compare_call(cfg, r, groups, idx, out, sent, owned, oS, oL, tag, state_ranks
                 c, q = payload_groups(r.sent[p][o], groups, bits)
                 assert_bits_equal(c, sent[p][o][0], f"{tag} sent codes {p}->{o}")
                 assert_bits_equal(q, sent[p][o][1], f"{tag} sent params {p}->{o}")
-        assert_bits_equal(gather_elems(r.S[p], idx), oS[p], f"{tag} S rank {p}")
-        assert_bits_equal(gather_elems(r.L[p], idx), oL[p], f"{tag} L rank {p}")
+        S, L = gather_state(r.state[p], idx)
+        assert_bits_equal(S, oS[p], f"{tag} S rank {p}")
+        assert_bits_equal(L, oL[p], f"{tag} L rank {p}")
 
 
 def run_chain(w, cfg_of_site, nsample, seed, full=False, state_ranks=(0,)):
