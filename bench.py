@@ -14,6 +14,7 @@ the algorithmic bytes per step over MI355X's 8 TB/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        python bench.py --copy-calibration BYTES     (plain copy for PMC scaling)
+       python bench.py --summarize-profiles DIR     (rocprofv3 CSVs -> profiles/)
 """
 from __future__ import annotations
 
@@ -81,6 +82,93 @@ def traffic_from_profile(workload: str, kernel: str):
     fr = c["bytes_read"] / (c["fetch_kib"] * 1024.0)
     fw = c["bytes_written"] / (c["write_kib"] * 1024.0)
     return k["fetch_kib"] * 1024.0 * fr + k["write_kib"] * 1024.0 * fw
+
+
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats --output-format csv -d DIR/prof_trace -o bench -- "
+             "python3 bench.py --steps 10 --warmup 2 --no-cpu-baseline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_FETCH_SIZE -o bench -- "
+             "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline",
+    "write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_WRITE_SIZE -o bench -- "
+             "python3 bench.py --steps 2 --warmup 0 --no-cpu-baseline",
+    "copy_fetch": "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_copy_FETCH_SIZE -o copy -- "
+                  "python3 bench.py --copy-calibration 1073741824",
+    "copy_write": "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/pmc_copy_WRITE_SIZE -o copy -- "
+                  "python3 bench.py --copy-calibration 1073741824",
+}
+
+
+def _kernel_key(name: str) -> str:
+    base = name.split("(")[0].split("<")[0]
+    return base.replace("void ", "").split("::")[-1]
+
+
+def summarize_profiles(d: str, workload: str = "msg1gib_p8", copy_bytes: int = 1 << 30):
+    """Reduce the rocprofv3 CSVs of PROFILE_COMMANDS (run from the repository
+    root on the GPU machine, DIR = their output folder) to profiles/."""
+    import csv
+    from collections import defaultdict
+    from error_compensated_bit_amd import binding as B
+    from error_compensated_bit_amd.inputs import WORKLOADS
+
+    def counters(path):
+        acc = defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            acc[_kernel_key(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fetch, nf = counters(os.path.join(d, "pmc_FETCH_SIZE", "bench_counter_collection.csv"))
+    write, _ = counters(os.path.join(d, "pmc_WRITE_SIZE", "bench_counter_collection.csv"))
+    cfetch, _ = counters(os.path.join(d, "pmc_copy_FETCH_SIZE", "copy_counter_collection.csv"))
+    cwrite, _ = counters(os.path.join(d, "pmc_copy_WRITE_SIZE", "copy_counter_collection.csv"))
+    copy_key = next(k for k in cfetch if "copy" in k.lower())   # the copy, not the fill before it
+    trace = {}
+    for r in csv.DictReader(open(os.path.join(d, "prof_trace", "bench_kernel_stats.csv"))):
+        trace[_kernel_key(r["Name"])] = {"calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                                         "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    w = WORKLOADS[workload]
+    alg = algorithmic_bytes(w.P, w.n, w.bits(0), 4)
+    out = {
+        "workload": workload,
+        "kernel_source_digest": kernel_source_digest(),
+        "commands": PROFILE_COMMANDS,
+        "copy_calibration": {"kernel": copy_key, "bytes_read": copy_bytes, "bytes_written": copy_bytes,
+                             "fetch_kib": cfetch[copy_key], "write_kib": cwrite[copy_key]},
+        "kernels": {k: {"fetch_kib": fetch[k], "write_kib": write[k], "dispatches": nf[k]}
+                    for k in KERNELS if k in fetch},
+        "trace": {k: trace[k] for k in KERNELS if k in trace},
+    }
+    os.makedirs(os.path.join(HERE, "profiles"), exist_ok=True)
+    json.dump(out, open(os.path.join(HERE, "profiles", f"pmc_{workload}.json"), "w"), indent=1)
+    fr = copy_bytes / (cfetch[copy_key] * 1024)
+    fw = copy_bytes / (cwrite[copy_key] * 1024)
+    lines = [f"# Kernel profile: one rank's share, {w.description}",
+             "",
+             f"Kernel source digest `{out['kernel_source_digest']}` (sources + hipcc flags, "
+             "`bench.py kernel_source_digest()`). Commands, run from the repository root with "
+             "`cd /tmp && export TMPDIR=/tmp` first (DIR = output folder):",
+             ""]
+    lines += [f"- {k}: `{v}`" for k, v in PROFILE_COMMANDS.items()]
+    lines += ["", f"Reduced with `python bench.py --summarize-profiles DIR`. Copy calibration "
+              f"(`{copy_key}`, {copy_bytes} B read and written): FETCH_SIZE reads "
+              f"{cfetch[copy_key]:.0f} KiB (read factor {fr:.4f}), WRITE_SIZE "
+              f"{cwrite[copy_key]:.0f} KiB (write factor {fw:.4f}).", "",
+              "| kernel | trace avg µs (calls) | algorithmic GB | HBM read GB | HBM write GB | "
+              "HBM total / algorithmic | algorithmic GB/s at trace avg | % of 8 TB/s |",
+              "|---|---|---|---|---|---|---|---|"]
+    for k in KERNELS:
+        if k not in fetch or k not in trace:
+            continue
+        rd = fetch[k] * 1024 * fr
+        wr = write[k] * 1024 * fw
+        t = trace[k]["avg_us"]
+        lines.append(f"| `{k}` | {t:.1f} ({trace[k]['calls']}) | {alg[k] / 1e9:.4f} | {rd / 1e9:.4f} | "
+                     f"{wr / 1e9:.4f} | {(rd + wr) / alg[k]:.4f} | {alg[k] / t / 1e3:.1f} | "
+                     f"{alg[k] / t / 1e3 / HBM_PEAK_GBS:.1%} |")
+    lines += ["", "Counter values are means over all dispatches of a kernel (the set-up call over "
+              "all ranks and the timed rank-0 steps have the same sizes)."]
+    open(os.path.join(HERE, "profiles", f"kernels_{workload}.md"), "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def copy_calibration(nbytes: int):
@@ -152,7 +240,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-den", type=int, default=4)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
+    ap.add_argument("--summarize-profiles", metavar="DIR")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the all-reduce (the other ranks are "

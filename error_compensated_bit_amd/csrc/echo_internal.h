@@ -14,8 +14,8 @@ constexpr int kInBF16 = 0, kInF16 = 1;
 constexpr int kOutBF16 = 0, kOutF32 = 1;
 constexpr int kStateF32 = 0, kStateBF16 = 1;
 
-// Upper bound on blocks per launch; larger problems stride.
-constexpr uint64_t kGridCap = 1u << 20;
+// Upper bound on blocks of the state-reset fill; larger arrays stride.
+constexpr uint64_t kZeroGridCap = 1u << 20;
 
 // Payload pointers of every segment, passed by value as kernel arguments.
 struct SegTable {

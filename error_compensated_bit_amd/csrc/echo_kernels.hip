@@ -261,7 +261,8 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
 // ------------------------------------------------------------------ K1
 // Entry pass of `rank` ([JP-1]: only the segments this rank does not own are
 // quantized; [JP-2]: feedback-add, residual and state update fused here).
-// grid.y = P-1 non-owned segments, grid.x covers the segment's groups.
+// grid.y = P-1 non-owned segments, grid.x covers the segment's groups, one
+// group per wave (fp32 state) or half-wave (bf16 state).
 template <int BITS, int IN_T, int ST_T, bool NT>
 __global__ __launch_bounds__(kThreads) void k_quant_feedback(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable out, int rank,
@@ -273,9 +274,10 @@ __global__ __launch_bounds__(kThreads) void k_quant_feedback(
   const uint64_t base = (uint64_t)p * seg_len;
   uint8_t* __restrict__ codes = static_cast<uint8_t*>(out.codes[p]);
   uint32_t* __restrict__ params = out.params[p];
-  const uint32_t gl = threadIdx.x / M::kLanes, lane = threadIdx.x % M::kLanes;
-  for (uint32_t g = blockIdx.x * M::kGroupsPerBlock + gl; g < groups;
-       g += gridDim.x * M::kGroupsPerBlock) {
+  const uint32_t lane = threadIdx.x % M::kLanes;
+  const uint32_t g = blockIdx.x * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
+  if (g >= groups) return;   // whole groups only: the lanes of a group leave together
+  {
     const uint64_t k = (uint64_t)g * kGroup + lane * E;   // index within the segment
     const uint64_t e = base + k;
     float xv[E], s[E], l[E], v[E];
@@ -314,9 +316,10 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
   using M = GroupMap<ST_T>;
   constexpr int E = M::kEPL;
   const uint64_t base = (uint64_t)rank * seg_len;
-  const uint32_t gl = threadIdx.x / M::kLanes, lane = threadIdx.x % M::kLanes;
-  for (uint32_t g = blockIdx.x * M::kGroupsPerBlock + gl; g < groups;
-       g += gridDim.x * M::kGroupsPerBlock) {
+  const uint32_t lane = threadIdx.x % M::kLanes;
+  const uint32_t g = blockIdx.x * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
+  if (g >= groups) return;
+  {
     const uint64_t k = (uint64_t)g * kGroup + lane * E;
     const uint64_t e = base + k;
     // incoming payload words first, so that all loads are in flight together
@@ -374,21 +377,33 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
 
 // ------------------------------------------------------------------ K3
 // Dequantize the P owners' payloads into the output ([JP-1]).
-// bf16 output: 8 elements per lane (one 16-byte store), 16 lanes per group;
-// fp32 output: 4 elements per lane (one 16-byte store), 32 lanes per group.
-template <int BITS, int OUT_T, bool NT>
+// EPL elements per lane and chunk (8 for bf16 output, 4 for fp32: one 16-byte
+// store either way), LPG = 128/EPL lanes per group, so a wave covers 64/LPG
+// groups per chunk; each lane does CH chunks, one wave-width (64*EPL
+// elements) apart, so every store instruction is 1 KiB contiguous.
+template <int OUT_T>
+struct GatherMap {
+  static constexpr int kEPL = (OUT_T == kOutBF16) ? 8 : 4;
+  static constexpr int kLanes = kGroup / kEPL;
+  static constexpr int kGroupsPerWave = 64 / kLanes;
+};
+
+template <int BITS, int OUT_T, int CH, bool NT>
 __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32_t groups,
                                                              uint64_t seg_len, void* __restrict__ out) {
-  constexpr int EPL = (OUT_T == kOutBF16) ? 8 : 4;
-  constexpr int LPG = kGroup / EPL;
-  constexpr int GPB = kThreads / LPG;
+  using M = GatherMap<OUT_T>;
+  constexpr int EPL = M::kEPL;
   const int p = blockIdx.y;
   const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(in.codes[p]);
   const uint32_t* __restrict__ params = in.params[p];
   const uint64_t base = (uint64_t)p * seg_len;
-  const uint32_t gl = threadIdx.x / LPG, lane = threadIdx.x % LPG;
-  for (uint32_t g = blockIdx.x * GPB + gl; g < groups; g += gridDim.x * GPB) {
-    const uint64_t k = (uint64_t)g * kGroup + lane * EPL;
+  const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const uint32_t g0 = (blockIdx.x * (kThreads / 64) + wave) * M::kGroupsPerWave * CH;
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) {
+    const uint32_t g = g0 + ch * M::kGroupsPerWave + lane / M::kLanes;
+    if (g >= groups) break;   // lanes are independent here
+    const uint64_t k = (uint64_t)g * kGroup + (lane % M::kLanes) * EPL;
     const uint32_t pw = params[g];
     const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
     float d[EPL];
@@ -441,13 +456,10 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint8_t* __restrict__ a, uint
 // ------------------------------------------------------------------ launchers
 namespace {
 
-// Blocks along x: `grid_x` when given, else enough for one group per lane
-// run (capped, so very large segments stride).
-unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned ny, unsigned grid_x) {
+// Blocks along x: `grid_x` when given, else one launch slot per group.
+unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned grid_x) {
   if (grid_x) return grid_x;
-  const uint64_t want = (groups + groups_per_block - 1) / groups_per_block;
-  const uint64_t cap = (kGridCap + ny - 1) / ny;
-  const uint64_t b = want < cap ? want : cap;
+  const uint64_t b = (groups + groups_per_block - 1) / groups_per_block;
   return (unsigned)(b == 0 ? 1 : b);
 }
 
@@ -457,7 +469,7 @@ template <int BITS, int IN_T, int ST_T, bool NT>
 void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
   const unsigned ny = (unsigned)(a.P - 1);
-  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, ny, grid_x), ny);
+  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, grid_x), ny);
   hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, NT>), grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
                      (uint32_t)groups, a.seg_len, a.coef);
@@ -466,25 +478,26 @@ void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
 template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT>
 void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
-  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, 1, grid_x));
+  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, grid_x));
   hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, NT>), grid,
                      dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, a.segs,
                      a.P, a.rank, (uint32_t)groups, a.seg_len,
                      static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
 }
 
-template <int BITS, int OUT_T, bool NT>
+template <int BITS, int OUT_T, int CH, bool NT>
 void launch_k3(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
-  constexpr int gpb = kThreads / (kGroup / ((OUT_T == kOutBF16) ? 8 : 4));
-  const unsigned ny = (unsigned)a.P;
-  dim3 grid(blocks_for(groups, gpb, ny, grid_x), ny);
-  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, NT>), grid, dim3(kThreads), 0, st, a.segs,
+  constexpr int gpb = (kThreads / 64) * GatherMap<OUT_T>::kGroupsPerWave * CH;
+  dim3 grid(blocks_for(groups, gpb, grid_x), (unsigned)a.P);
+  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, CH, NT>), grid, dim3(kThreads), 0, st, a.segs,
                      (uint32_t)groups, a.seg_len, a.out);
 }
 
-// Nontemporal loads and stores for every streamed array.
+// Nontemporal loads and stores for every streamed array; chunks per lane of
+// the gather pass.
 constexpr bool kNT = true;
+constexpr int kGatherChunks = 2;
 
 // Runtime -> template dispatch.
 void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
@@ -510,16 +523,17 @@ void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
 }
 
 void run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
-  if (a.bits == 4 && a.out_dtype == kOutBF16) return launch_k3<4, kOutBF16, kNT>(a, 0, st);
-  if (a.bits == 4 && a.out_dtype == kOutF32) return launch_k3<4, kOutF32, kNT>(a, 0, st);
-  if (a.bits == 8 && a.out_dtype == kOutBF16) return launch_k3<8, kOutBF16, kNT>(a, 0, st);
-  if (a.bits == 8 && a.out_dtype == kOutF32) return launch_k3<8, kOutF32, kNT>(a, 0, st);
+  constexpr int C = kGatherChunks;
+  if (a.bits == 4 && a.out_dtype == kOutBF16) return launch_k3<4, kOutBF16, C, kNT>(a, 0, st);
+  if (a.bits == 4 && a.out_dtype == kOutF32) return launch_k3<4, kOutF32, C, kNT>(a, 0, st);
+  if (a.bits == 8 && a.out_dtype == kOutBF16) return launch_k3<8, kOutBF16, C, kNT>(a, 0, st);
+  if (a.bits == 8 && a.out_dtype == kOutF32) return launch_k3<8, kOutF32, C, kNT>(a, 0, st);
 }
 
 void run_zero(void* p, uint64_t bytes, hipStream_t st) {
   const uint64_t n16 = bytes / 16;
   uint64_t blocks = (n16 + kThreads - 1) / kThreads;
-  if (blocks > kGridCap) blocks = kGridCap;
+  if (blocks > kZeroGridCap) blocks = kZeroGridCap;
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(kThreads), 0, st,
                      static_cast<uint8_t*>(p), bytes);
