@@ -239,6 +239,17 @@ __device__ __forceinline__ float feedback(float x, float s, float l, float eta) 
 }
 
 constexpr int kThreads = 256;
+constexpr uint32_t kXcds = 8;   // MI355X: 8 accelerator dies, each with its own L2
+
+// Blocks are dealt to the XCDs round-robin in launch order.  Renumber them so
+// that each XCD works through one contiguous range of the grid: data that
+// neighbouring blocks share at sub-line granularity (the 4-byte group
+// parameters, 32 groups per 128-byte line) then stays in one L2.
+__device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t b, uint32_t nb) {
+  const uint32_t q = nb / kXcds, r = nb % kXcds;
+  const uint32_t x = b % kXcds, i = b / kXcds;
+  return x * q + (x < r ? x : r) + i;
+}
 
 // Mapping of one 128-group onto lanes for a state type (see the file header).
 template <int ST_T>
@@ -263,19 +274,24 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
 // quantized; [JP-2]: feedback-add, residual and state update fused here).
 // grid.y = P-1 non-owned segments, grid.x covers the segment's groups, one
 // group per wave (fp32 state) or half-wave (bf16 state).
-template <int BITS, int IN_T, int ST_T, bool NT>
+template <int BITS, int IN_T, int ST_T, bool NT, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_quant_feedback(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable out, int rank,
     uint32_t groups, uint64_t seg_len, Coef c) {
   using M = GroupMap<ST_T>;
   constexpr int E = M::kEPL;
-  const int slot = blockIdx.y;
-  const int p = slot + (slot >= rank ? 1 : 0);
+  uint32_t bx = blockIdx.x, slot = blockIdx.y;
+  if constexpr (XCD) {
+    const uint32_t L = xcd_contiguous_block(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+    slot = L / gridDim.x;
+    bx = L - slot * gridDim.x;
+  }
+  const int p = (int)slot + ((int)slot >= rank ? 1 : 0);
   const uint64_t base = (uint64_t)p * seg_len;
   uint8_t* __restrict__ codes = static_cast<uint8_t*>(out.codes[p]);
   uint32_t* __restrict__ params = out.params[p];
   const uint32_t lane = threadIdx.x % M::kLanes;
-  const uint32_t g = blockIdx.x * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
+  const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
   if (g >= groups) return;   // whole groups only: the lanes of a group leave together
   {
     const uint64_t k = (uint64_t)g * kGroup + lane * E;   // index within the segment
@@ -308,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_feedback(
 // Owner pass over segment `rank` ([JP-1]: sum in fp32 in rank order with the
 // owner's own unquantized term, requantize; [JP-W] the round trip; [JP-2]
 // the owner's residual against the output value, state update fused).
-template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT>
+template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT, bool NTP, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable in, int P, int rank,
     uint32_t groups, uint64_t seg_len, uint8_t* __restrict__ out_codes,
@@ -317,7 +333,8 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
   constexpr int E = M::kEPL;
   const uint64_t base = (uint64_t)rank * seg_len;
   const uint32_t lane = threadIdx.x % M::kLanes;
-  const uint32_t g = blockIdx.x * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
+  const uint32_t bx = XCD ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
+  const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
   if (g >= groups) return;
   {
     const uint64_t k = (uint64_t)g * kGroup + lane * E;
@@ -327,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
 #pragma unroll
     for (int p = 0; p < kMaxRanks; ++p) {
       if (p < P && p != rank) {
-        cw[p] = CodeIO<BITS, E>::template load<NT>(static_cast<const uint8_t*>(in.codes[p]), k);
+        cw[p] = CodeIO<BITS, E>::template load<NTP>(static_cast<const uint8_t*>(in.codes[p]), k);
         pw[p] = in.params[p][g];
       }
     }
@@ -388,7 +405,7 @@ struct GatherMap {
   static constexpr int kGroupsPerWave = 64 / kLanes;
 };
 
-template <int BITS, int OUT_T, int CH, bool NT>
+template <int BITS, int OUT_T, int CH, bool NT, bool NTP>
 __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32_t groups,
                                                              uint64_t seg_len, void* __restrict__ out) {
   using M = GatherMap<OUT_T>;
@@ -408,22 +425,22 @@ __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32
     const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
     float d[EPL];
     if constexpr (BITS == 4 && EPL == 8) {
-      const uint32_t w = ld<NT>(reinterpret_cast<const uint32_t*>(codes + k / 2));
+      const uint32_t w = ld<NTP>(reinterpret_cast<const uint32_t*>(codes + k / 2));
 #pragma unroll
       for (int i = 0; i < 8; ++i) d[i] = decode((w >> (4 * i)) & 0xfu, sf, zf);
     } else if constexpr (BITS == 4) {
-      const uint32_t w = ld<NT>(reinterpret_cast<const uint16_t*>(codes + k / 2));
+      const uint32_t w = ld<NTP>(reinterpret_cast<const uint16_t*>(codes + k / 2));
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = decode((w >> (4 * i)) & 0xfu, sf, zf);
     } else if constexpr (EPL == 8) {
-      const u32x2 w = ld<NT>(reinterpret_cast<const u32x2*>(codes + k));
+      const u32x2 w = ld<NTP>(reinterpret_cast<const u32x2*>(codes + k));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         d[i] = decode((w.x >> (8 * i)) & 0xffu, sf, zf);
         d[4 + i] = decode((w.y >> (8 * i)) & 0xffu, sf, zf);
       }
     } else {
-      const uint32_t w = ld<NT>(reinterpret_cast<const uint32_t*>(codes + k));
+      const uint32_t w = ld<NTP>(reinterpret_cast<const uint32_t*>(codes + k));
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = decode((w >> (8 * i)) & 0xffu, sf, zf);
     }
@@ -465,44 +482,51 @@ unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned grid_x)
 
 }  // namespace
 
-template <int BITS, int IN_T, int ST_T, bool NT>
+template <int BITS, int IN_T, int ST_T, bool NT, bool XCD>
 void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
   const unsigned ny = (unsigned)(a.P - 1);
   dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, grid_x), ny);
-  hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, NT>), grid, dim3(kThreads), 0, st,
+  hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, NT, XCD>), grid, dim3(kThreads), 0, st,
                      static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
                      (uint32_t)groups, a.seg_len, a.coef);
 }
 
-template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT>
+template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT, bool NTP, bool XCD>
 void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
   dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, grid_x));
-  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, NT>), grid,
+  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, NT, NTP, XCD>), grid,
                      dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, a.segs,
                      a.P, a.rank, (uint32_t)groups, a.seg_len,
                      static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
 }
 
-template <int BITS, int OUT_T, int CH, bool NT>
+template <int BITS, int OUT_T, int CH, bool NT, bool NTP>
 void launch_k3(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / kGroup;
   constexpr int gpb = (kThreads / 64) * GatherMap<OUT_T>::kGroupsPerWave * CH;
   dim3 grid(blocks_for(groups, gpb, grid_x), (unsigned)a.P);
-  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, CH, NT>), grid, dim3(kThreads), 0, st, a.segs,
+  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, CH, NT, NTP>), grid, dim3(kThreads), 0, st, a.segs,
                      (uint32_t)groups, a.seg_len, a.out);
 }
 
 // Nontemporal loads and stores for every streamed array; chunks per lane of
 // the gather pass.
+// The owner pass reads its P-1 incoming payloads with ordinary loads: the two
+// halves of a 128-byte code line belong to neighbouring waves of one block,
+// and a nontemporal first read makes the second fetch the line again.
 constexpr bool kNT = true;
+constexpr bool kNTOwnerPayload = false;
+// XCD-contiguous block order: the owner pass reads P-1 parameter arrays at 4
+// bytes per group and gains from it; the entry pass measured slightly slower.
+constexpr bool kXcdOrderEntry = false, kXcdOrderOwner = true;
 constexpr int kGatherChunks = 2;
 
 // Runtime -> template dispatch.
 void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
 #define ECHO_K1(B, I, S) \
-  if (a.bits == B && a.in_dtype == I && a.state_dtype == S) return launch_k1<B, I, S, kNT>(a, 0, st);
+  if (a.bits == B && a.in_dtype == I && a.state_dtype == S) return launch_k1<B, I, S, kNT, kXcdOrderEntry>(a, 0, st);
   ECHO_K1(4, kInBF16, kStateF32) ECHO_K1(4, kInBF16, kStateBF16)
   ECHO_K1(4, kInF16, kStateF32)  ECHO_K1(4, kInF16, kStateBF16)
   ECHO_K1(8, kInBF16, kStateF32) ECHO_K1(8, kInBF16, kStateBF16)
@@ -513,7 +537,7 @@ void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
 void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
 #define ECHO_K2(B, I, S, O)                                                      \
   if (a.bits == B && a.in_dtype == I && a.state_dtype == S && a.out_dtype == O) \
-    return launch_k2<B, I, S, O, kNT>(a, 0, st);
+    return launch_k2<B, I, S, O, kNT, kNTOwnerPayload, kXcdOrderOwner>(a, 0, st);
 #define ECHO_K2_IO(B, I) \
   ECHO_K2(B, I, kStateF32, kOutBF16) ECHO_K2(B, I, kStateF32, kOutF32) \
   ECHO_K2(B, I, kStateBF16, kOutBF16) ECHO_K2(B, I, kStateBF16, kOutF32)
@@ -524,10 +548,10 @@ void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
 
 void run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
   constexpr int C = kGatherChunks;
-  if (a.bits == 4 && a.out_dtype == kOutBF16) return launch_k3<4, kOutBF16, C, kNT>(a, 0, st);
-  if (a.bits == 4 && a.out_dtype == kOutF32) return launch_k3<4, kOutF32, C, kNT>(a, 0, st);
-  if (a.bits == 8 && a.out_dtype == kOutBF16) return launch_k3<8, kOutBF16, C, kNT>(a, 0, st);
-  if (a.bits == 8 && a.out_dtype == kOutF32) return launch_k3<8, kOutF32, C, kNT>(a, 0, st);
+  if (a.bits == 4 && a.out_dtype == kOutBF16) return launch_k3<4, kOutBF16, C, kNT, kNT>(a, 0, st);
+  if (a.bits == 4 && a.out_dtype == kOutF32) return launch_k3<4, kOutF32, C, kNT, kNT>(a, 0, st);
+  if (a.bits == 8 && a.out_dtype == kOutBF16) return launch_k3<8, kOutBF16, C, kNT, kNT>(a, 0, st);
+  if (a.bits == 8 && a.out_dtype == kOutF32) return launch_k3<8, kOutF32, C, kNT, kNT>(a, 0, st);
 }
 
 void run_zero(void* p, uint64_t bytes, hipStream_t st) {
