@@ -12,7 +12,8 @@ value = effective all-reduce bandwidth = 2 bytes * n / step time (16-bit
 input bytes per second), the metric the method is quoted on; hbm_frac is
 the algorithmic bytes per step over MI355X's 8 TB/s.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--site S]
+                       [--state f32|bf16] [--graph]
        python bench.py --copy-calibration BYTES     (plain copy for PMC scaling)
        python bench.py --summarize-profiles DIR     (rocprofv3 CSVs -> profiles/)
 """
@@ -56,10 +57,11 @@ def algorithmic_bytes(P: int, n: int, bits: int, state_bytes: int, in_bytes=2, o
 
 
 def kernel_source_digest() -> str:
-    """Digest of everything that determines the kernels' code."""
+    """Digest of what determines the kernels' code: their source, the header
+    they include and the compiler flags (not the argument-checking layer)."""
     from error_compensated_bit_amd import build as eb
     h = hashlib.sha256()
-    for f in eb.SOURCES + eb.HEADERS:
+    for f in (os.path.join(eb.CSRC, "echo_kernels.hip"), os.path.join(eb.CSRC, "echo_internal.h")):
         h.update(open(f, "rb").read())
     h.update(" ".join(eb.hipcc_flags()).encode())
     return h.hexdigest()[:16]
@@ -190,7 +192,7 @@ def cpu_baseline(cfg, w, xs_dev, frac_den: int):
     from error_compensated_bit_amd.inputs import bits16_numpy
     P, n = w.P, w.n
     seg = n // P
-    sseg = seg // frac_den
+    sseg = max(128, (seg // frac_den) // 128 * 128)
     ns = sseg * P
     xs = []
     for x in xs_dev:
@@ -222,7 +224,7 @@ def cpu_baseline(cfg, w, xs_dev, frac_den: int):
     t_share = t_entry / P + t_owner / P + t_gather
     return {"value": round(2.0 * ns / t_share / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"first 1/{frac_den} of every segment ({ns} of {n} elements per rank), "
+            "sample": f"first {sseg} elements of every segment ({ns} of {n} elements per rank), "
                       f"all {P} ranks, one call; share time {t_share:.2f} s "
                       f"(entry {t_entry / P:.2f} + owner {t_owner / P:.2f} + gather {t_gather:.2f}); "
                       f"single-threaded scalar C, total CPU time "
@@ -236,9 +238,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="msg1gib_p8")
     ap.add_argument("--rank", type=int, default=0)
+    ap.add_argument("--site", type=int, default=0,
+                    help="call of a chained workload whose inputs and width are used")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step captured in a HIP graph (launch-bound messages)")
     ap.add_argument("--state", choices=("f32", "bf16"), default="f32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-den", type=int, default=4)
+    ap.add_argument("--cpu-sample-den", type=int, default=0,
+                    help="oracle sample = 1/DEN of every segment (default: about 10 s of CPU work)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES")
     ap.add_argument("--summarize-profiles", metavar="DIR")
     args = ap.parse_args()
@@ -264,15 +271,15 @@ def main():
     B.load_library()
     w = WORKLOADS[args.workload]
     P, n = w.P, w.n
-    bits = w.bits(0)
+    bits = w.bits(args.site)
     sdt = B.ECHO_STATE_F32 if args.state == "f32" else B.ECHO_STATE_BF16
     cfg = B.make_config(bits=bits, state_dtype=sdt)
     dev = "cuda:0"
-    log(f"workload {w.name}: {w.description}; rank {args.rank} of {P}, n={n}, bits={bits}, "
-        f"state={args.state}")
+    log(f"workload {w.name}: {w.description}; site {args.site}, rank {args.rank} of {P}, n={n}, "
+        f"bits={bits}, state={args.state}")
 
     t_setup = time.perf_counter()
-    xs = [make_x(w, 0, p, device=dev) for p in range(P)]
+    xs = [make_x(w, args.site, p, device=dev) for p in range(P)]
     r = sim.alloc_ranks(cfg, P, n, dev)
     sim.allreduce(cfg, r, xs)          # every rank's payloads exist before timing
     torch.cuda.synchronize()
@@ -308,6 +315,26 @@ def main():
     k_ms = {k: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
             for j, k in enumerate(KERNELS)}
     ms_per_step = wall * 1e3 / args.steps
+    ms_eager = ms_per_step
+    ms_graph = None
+    if args.graph:
+        # the same three launches captured once and replayed (no memset nodes)
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            stream = torch.cuda.current_stream()
+            step()
+        stream = torch.cuda.current_stream()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms_per_step = ms_graph
+        log(f"  step {ms_graph:.4f} ms wall as a graph replay (eager {ms_eager:.4f} ms)")
     alg = algorithmic_bytes(P, n, bits, 4 if sdt == B.ECHO_STATE_F32 else 2)
     alg_total = sum(alg.values())
     for k in KERNELS:
@@ -333,12 +360,15 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "hbm_frac": round(alg_total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "config": {"workload": w.name, "P": P, "n_per_rank": n, "rank": rank, "bits": bits,
+        "config": {"workload": w.name, "site": args.site, "P": P, "n_per_rank": n, "rank": rank,
+                   "bits": bits,
                    "group": 128, "state": args.state, "input": "bf16", "output": "bf16",
                    "eta": cfg.eta, "beta_short": cfg.beta_short, "beta_long": cfg.beta_long,
                    "mix_long": round(cfg.mix_long, 6),
                    "algorithmic_bytes_per_step": int(alg_total)},
         "kernel_ms": {k: round(v, 5) for k, v in k_ms.items()},
+        "ms_per_step_eager": round(ms_eager, 5),
+        "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else int(traffic),
@@ -346,7 +376,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a sample ...")
-        line["cpu_baseline"] = cpu_baseline(cfg, w, xs, args.cpu_sample_den)
+        den = args.cpu_sample_den or max(1, round(n * P / 5.4e8))
+        line["cpu_baseline"] = cpu_baseline(cfg, w, xs, den)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

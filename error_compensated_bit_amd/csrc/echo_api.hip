@@ -29,12 +29,13 @@ int check_config(const echo_config* c) {
 }
 
 // P ranks, message of n elements: n must be a positive multiple of P*group,
-// and a segment must fit the kernels' 32-bit group counter.
+// and a segment may hold at most 2^31 groups (the kernels' 32-bit group
+// index then cannot wrap).
 int check_shape(int P, int64_t n) {
   if (P < 1 || P > ECHO_MAX_RANKS) return ECHO_ERR_ARG;
   if (n <= 0) return ECHO_ERR_SHAPE;
   if (n % ((int64_t)P * ECHO_GROUP) != 0) return ECHO_ERR_SHAPE;
-  if (n / P / ECHO_GROUP > (int64_t)UINT32_MAX) return ECHO_ERR_SHAPE;
+  if (n / P / ECHO_GROUP > ((int64_t)1 << 31)) return ECHO_ERR_SHAPE;
   return ECHO_OK;
 }
 

@@ -62,7 +62,7 @@ extern "C" {
 /* return codes */
 #define ECHO_OK          0
 #define ECHO_ERR_ARG    -1   /* null pointer, unsupported or out-of-range parameter */
-#define ECHO_ERR_SHAPE  -2   /* n not a positive multiple of P * group */
+#define ECHO_ERR_SHAPE  -2   /* n not a positive multiple of P * group, or n/P > 2^31 groups */
 #define ECHO_ERR_ALIGN  -3   /* a buffer pointer is not 16-byte aligned */
 #define ECHO_ERR_HIP    -4   /* the HIP runtime reported an error at launch */
 

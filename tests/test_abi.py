@@ -84,6 +84,8 @@ def cfg(**kw):
     (lambda L: L.echo_quantize_feedback(cfg(), 2, -1, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 0, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 384, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 2 * 128 * ((1 << 31) + 1), A, A, SEGS, None),
+     B.ECHO_ERR_SHAPE),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, None, A, SEGS, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A + 8, A, SEGS, None), B.ECHO_ERR_ALIGN),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A + 4, SEGS, None), B.ECHO_ERR_ALIGN),
