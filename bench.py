@@ -42,13 +42,14 @@ def payload_bytes_per_elem(bits: int, group: int = 128) -> float:
     return bits / 8 + 4 / group
 
 
-def algorithmic_bytes(P: int, n: int, bits: int, state_bytes: int, in_bytes=2, out_bytes=2):
+def algorithmic_bytes(P: int, n: int, bits: int, state_bytes: int, in_bytes=2, out_bytes=2,
+                      group: int = 128):
     """Bytes each kernel must move per launch (one rank's share):
     entry: (P-1)/P of x, S and L read, S and L written, P-1 payloads written;
     owner: 1/P of x, S, L read and S, L written, P-1 payloads read, one written;
     gather: P payloads read, n outputs written."""
     seg = n // P
-    pb = payload_bytes_per_elem(bits)
+    pb = payload_bytes_per_elem(bits, group)
     st = 4 * state_bytes   # S and L, read and written
     k1 = (P - 1) * seg * (in_bytes + st + pb)
     k2 = seg * (in_bytes + st + (P - 1) * pb + pb)
@@ -243,6 +244,7 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="also time the step captured in a HIP graph (launch-bound messages)")
     ap.add_argument("--state", choices=("f32", "bf16"), default="f32")
+    ap.add_argument("--group", type=int, choices=(32, 64, 128), default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-den", type=int, default=0,
                     help="oracle sample = 1/DEN of every segment (default: about 10 s of CPU work)")
@@ -273,7 +275,7 @@ def main():
     P, n = w.P, w.n
     bits = w.bits(args.site)
     sdt = B.ECHO_STATE_F32 if args.state == "f32" else B.ECHO_STATE_BF16
-    cfg = B.make_config(bits=bits, state_dtype=sdt)
+    cfg = B.make_config(bits=bits, state_dtype=sdt, group=args.group)
     dev = "cuda:0"
     log(f"workload {w.name}: {w.description}; site {args.site}, rank {args.rank} of {P}, n={n}, "
         f"bits={bits}, state={args.state}")
@@ -335,7 +337,7 @@ def main():
         ms_graph = (time.perf_counter() - t0) * 1e3 / args.steps
         ms_per_step = ms_graph
         log(f"  step {ms_graph:.4f} ms wall as a graph replay (eager {ms_eager:.4f} ms)")
-    alg = algorithmic_bytes(P, n, bits, 4 if sdt == B.ECHO_STATE_F32 else 2)
+    alg = algorithmic_bytes(P, n, bits, 4 if sdt == B.ECHO_STATE_F32 else 2, group=args.group)
     alg_total = sum(alg.values())
     for k in KERNELS:
         log(f"  {k:24s} {k_ms[k]:8.4f} ms  {alg[k] / k_ms[k] / 1e6:8.1f} GB/s algorithmic "
@@ -362,7 +364,7 @@ def main():
         "hbm_frac": round(alg_total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "config": {"workload": w.name, "site": args.site, "P": P, "n_per_rank": n, "rank": rank,
                    "bits": bits,
-                   "group": 128, "state": args.state, "input": "bf16", "output": "bf16",
+                   "group": args.group, "state": args.state, "input": "bf16", "output": "bf16",
                    "eta": cfg.eta, "beta_short": cfg.beta_short, "beta_long": cfg.beta_long,
                    "mix_long": round(cfg.mix_long, 6),
                    "algorithmic_bytes_per_step": int(alg_total)},

@@ -111,9 +111,10 @@ def echo_state_bytes(n: int, state_dtype: int) -> int:
     return load_library().echo_state_bytes(n, state_dtype)
 
 
-def alloc_payload(seg_len: int, bits: int, device, fill: int | None = None) -> Payload:
+def alloc_payload(seg_len: int, bits: int, device, fill: int | None = None,
+                  group: int = ECHO_GROUP) -> Payload:
     """Payload buffers for seg_len elements; `fill` sets every byte (sentinels)."""
-    cb, pb = echo_codes_bytes(seg_len, bits), echo_params_bytes(seg_len)
+    cb, pb = echo_codes_bytes(seg_len, bits), echo_params_bytes(seg_len, group)
     if cb == 0 or pb == 0:
         raise ValueError(f"no payload layout for {seg_len} elements at {bits} bits")
     if fill is None:

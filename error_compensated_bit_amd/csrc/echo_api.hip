@@ -17,7 +17,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_config(const echo_config* c) {
   if (!c) return ECHO_ERR_ARG;
   if (c->bits != 4 && c->bits != 8) return ECHO_ERR_ARG;
-  if (c->group != ECHO_GROUP) return ECHO_ERR_ARG;
+  if (c->group != 32 && c->group != 64 && c->group != 128) return ECHO_ERR_ARG;
   if (c->in_dtype != ECHO_IN_BF16 && c->in_dtype != ECHO_IN_F16) return ECHO_ERR_ARG;
   if (c->out_dtype != ECHO_OUT_BF16 && c->out_dtype != ECHO_OUT_F32) return ECHO_ERR_ARG;
   if (c->state_dtype != ECHO_STATE_F32 && c->state_dtype != ECHO_STATE_BF16) return ECHO_ERR_ARG;
@@ -31,11 +31,11 @@ int check_config(const echo_config* c) {
 // P ranks, message of n elements: n must be a positive multiple of P*group,
 // and a segment may hold at most 2^31 groups (the kernels' 32-bit group
 // index then cannot wrap).
-int check_shape(int P, int64_t n) {
+int check_shape(int P, int64_t n, int group) {
   if (P < 1 || P > ECHO_MAX_RANKS) return ECHO_ERR_ARG;
   if (n <= 0) return ECHO_ERR_SHAPE;
-  if (n % ((int64_t)P * ECHO_GROUP) != 0) return ECHO_ERR_SHAPE;
-  if (n / P / ECHO_GROUP > ((int64_t)1 << 31)) return ECHO_ERR_SHAPE;
+  if (n % ((int64_t)P * group) != 0) return ECHO_ERR_SHAPE;
+  if (n / P / group > ((int64_t)1 << 31)) return ECHO_ERR_SHAPE;
   return ECHO_OK;
 }
 
@@ -67,6 +67,7 @@ LaunchArgs base_args(const echo_config* c, int P, int rank, int64_t n) {
   LaunchArgs a;
   memset(&a, 0, sizeof a);
   a.bits = c->bits;
+  a.group = c->group;
   a.in_dtype = c->in_dtype;
   a.out_dtype = c->out_dtype;
   a.state_dtype = c->state_dtype;
@@ -98,7 +99,7 @@ int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* strea
 int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n, const void* x,
                            void* state, const echo_seg* out, void* stream) {
   int rc;
-  if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
+  if ((rc = check_config(cfg)) || (rc = check_shape(P, n, cfg->group))) return rc;
   if (rank < 0 || rank >= P) return ECHO_ERR_ARG;
   if ((rc = check_buf(x)) || (rc = check_buf(state))) return rc;
   if (!out) return ECHO_ERR_ARG;
@@ -120,7 +121,7 @@ int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n
                               void* state, const echo_seg* in, const echo_seg* out,
                               void* stream) {
   int rc;
-  if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
+  if ((rc = check_config(cfg)) || (rc = check_shape(P, n, cfg->group))) return rc;
   if (rank < 0 || rank >= P) return ECHO_ERR_ARG;
   if ((rc = check_buf(x)) || (rc = check_buf(state))) return rc;
   if (!in && P > 1) return ECHO_ERR_ARG;
@@ -143,7 +144,7 @@ int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n
 int echo_dequant_gather(const echo_config* cfg, int P, int64_t n, const echo_seg* in, void* out,
                         void* stream) {
   int rc;
-  if ((rc = check_config(cfg)) || (rc = check_shape(P, n))) return rc;
+  if ((rc = check_config(cfg)) || (rc = check_shape(P, n, cfg->group))) return rc;
   if (!in) return ECHO_ERR_ARG;
   if ((rc = check_buf(out))) return rc;
   LaunchArgs a = base_args(cfg, P, 0, n);

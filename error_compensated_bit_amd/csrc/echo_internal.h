@@ -6,7 +6,6 @@
 
 namespace echo {
 
-constexpr int kGroup = 128;
 constexpr int kMaxRanks = 16;
 
 // element-type tags (same values as the ECHO_* constants of the public header)
@@ -31,7 +30,7 @@ struct Coef {
 };
 
 struct LaunchArgs {
-  int bits, in_dtype, out_dtype, state_dtype;
+  int bits, group, in_dtype, out_dtype, state_dtype;
   int P, rank;
   uint64_t seg_len;
   const void* x;

@@ -75,21 +75,6 @@ __device__ __forceinline__ float swz_xor16(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
 
-// Min and max over each 32-lane half of a wave; every lane of a half gets
-// its half's result.
-__device__ __forceinline__ void halfwave_minmax(float& mn, float& mx) {
-  mn = fminf(mn, dpp<kDppXor1>(mn));
-  mx = fmaxf(mx, dpp<kDppXor1>(mx));
-  mn = fminf(mn, dpp<kDppXor2>(mn));
-  mx = fmaxf(mx, dpp<kDppXor2>(mx));
-  mn = fminf(mn, dpp<kDppHalfMirror>(mn));
-  mx = fmaxf(mx, dpp<kDppHalfMirror>(mx));
-  mn = fminf(mn, dpp<kDppMirror>(mn));
-  mx = fmaxf(mx, dpp<kDppMirror>(mx));
-  mn = fminf(mn, swz_xor16(mn));
-  mx = fmaxf(mx, swz_xor16(mx));
-}
-
 // Combine the two already-reduced 32-lane halves of a wave (wave-uniform).
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
@@ -251,19 +236,35 @@ __device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t b, uint32_t nb
   return x * q + (x < r ? x : r) + i;
 }
 
-// Mapping of one 128-group onto lanes for a state type (see the file header).
-template <int ST_T>
+// Mapping of one group of G elements onto lanes for a state type (see the
+// file header): kLanes = G / EPL consecutive lanes, aligned runs.
+template <int ST_T, int G>
 struct GroupMap {
   static constexpr int kEPL = StateIO<ST_T>::kEPL;       // elements per lane
-  static constexpr int kLanes = kGroup / kEPL;            // lanes per group: 64 or 32
+  static constexpr int kLanes = G / kEPL;                 // lanes per group: 8 .. 64
   static constexpr int kGroupsPerBlock = kThreads / kLanes;
+  static_assert(kLanes == 8 || kLanes == 16 || kLanes == 32 || kLanes == 64, "lanes per group");
 };
 
-// Min and max of a group held by GroupMap<ST_T>::kLanes lanes; every lane gets them.
-template <int ST_T>
+// Min and max over each aligned run of LANES lanes; every lane of a run gets
+// its run's result.
+template <int LANES>
 __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
-  halfwave_minmax(mn, mx);
-  if constexpr (GroupMap<ST_T>::kLanes == 64) {
+  mn = fminf(mn, dpp<kDppXor1>(mn));
+  mx = fmaxf(mx, dpp<kDppXor1>(mx));
+  mn = fminf(mn, dpp<kDppXor2>(mn));
+  mx = fmaxf(mx, dpp<kDppXor2>(mx));
+  mn = fminf(mn, dpp<kDppHalfMirror>(mn));
+  mx = fmaxf(mx, dpp<kDppHalfMirror>(mx));
+  if constexpr (LANES >= 16) {
+    mn = fminf(mn, dpp<kDppMirror>(mn));
+    mx = fmaxf(mx, dpp<kDppMirror>(mx));
+  }
+  if constexpr (LANES >= 32) {
+    mn = fminf(mn, swz_xor16(mn));
+    mx = fmaxf(mx, swz_xor16(mx));
+  }
+  if constexpr (LANES == 64) {
     mn = fminf(lane_value(mn, 0), lane_value(mn, 32));
     mx = fmaxf(lane_value(mx, 0), lane_value(mx, 32));
   }
@@ -273,12 +274,12 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
 // Entry pass of `rank` ([JP-1]: only the segments this rank does not own are
 // quantized; [JP-2]: feedback-add, residual and state update fused here).
 // grid.y = P-1 non-owned segments, grid.x covers the segment's groups, one
-// group per wave (fp32 state) or half-wave (bf16 state).
-template <int BITS, int IN_T, int ST_T, bool NT, bool XCD>
+// group per run of G/EPL lanes.
+template <int BITS, int IN_T, int ST_T, int G, bool NT, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_quant_feedback(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable out, int rank,
     uint32_t groups, uint64_t seg_len, Coef c) {
-  using M = GroupMap<ST_T>;
+  using M = GroupMap<ST_T, G>;
   constexpr int E = M::kEPL;
   uint32_t bx = blockIdx.x, slot = blockIdx.y;
   if constexpr (XCD) {
@@ -294,7 +295,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_feedback(
   const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
   if (g >= groups) return;   // whole groups only: the lanes of a group leave together
   {
-    const uint64_t k = (uint64_t)g * kGroup + lane * E;   // index within the segment
+    const uint64_t k = (uint64_t)g * G + lane * E;   // index within the segment
     const uint64_t e = base + k;
     float xv[E], s[E], l[E], v[E];
     load_in<IN_T, E, NT>(x + e, xv);
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_feedback(
       mn = fminf(mn, v[i]);
       mx = fmaxf(mx, v[i]);
     }
-    group_minmax<ST_T>(mn, mx);
+    group_minmax<M::kLanes>(mn, mx);
     const QParams qp = group_params<BITS>(mn, mx);
     uint32_t q[E];
 #pragma unroll
@@ -324,12 +325,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_feedback(
 // Owner pass over segment `rank` ([JP-1]: sum in fp32 in rank order with the
 // owner's own unquantized term, requantize; [JP-W] the round trip; [JP-2]
 // the owner's residual against the output value, state update fused).
-template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT, bool NTP, bool XCD>
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable in, int P, int rank,
     uint32_t groups, uint64_t seg_len, uint8_t* __restrict__ out_codes,
     uint32_t* __restrict__ out_params, Coef c) {
-  using M = GroupMap<ST_T>;
+  using M = GroupMap<ST_T, G>;
   constexpr int E = M::kEPL;
   const uint64_t base = (uint64_t)rank * seg_len;
   const uint32_t lane = threadIdx.x % M::kLanes;
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
   const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
   if (g >= groups) return;
   {
-    const uint64_t k = (uint64_t)g * kGroup + lane * E;
+    const uint64_t k = (uint64_t)g * G + lane * E;
     const uint64_t e = base + k;
     // incoming payload words first, so that all loads are in flight together
     uint32_t cw[kMaxRanks], pw[kMaxRanks];
@@ -376,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
       mn = fminf(mn, acc[i]);
       mx = fmaxf(mx, acc[i]);
     }
-    group_minmax<ST_T>(mn, mx);
+    group_minmax<M::kLanes>(mn, mx);
     const QParams qp = group_params<BITS>(mn, mx);
     uint32_t q[E];
 #pragma unroll
@@ -395,20 +396,20 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
 // ------------------------------------------------------------------ K3
 // Dequantize the P owners' payloads into the output ([JP-1]).
 // EPL elements per lane and chunk (8 for bf16 output, 4 for fp32: one 16-byte
-// store either way), LPG = 128/EPL lanes per group, so a wave covers 64/LPG
-// groups per chunk; each lane does CH chunks, one wave-width (64*EPL
-// elements) apart, so every store instruction is 1 KiB contiguous.
-template <int OUT_T>
+// store either way), G/EPL lanes per group, so a wave covers 64*EPL/G groups
+// per chunk; each lane does CH chunks, one wave-width (64*EPL elements)
+// apart, so every store instruction is 1 KiB contiguous.
+template <int OUT_T, int G>
 struct GatherMap {
   static constexpr int kEPL = (OUT_T == kOutBF16) ? 8 : 4;
-  static constexpr int kLanes = kGroup / kEPL;
+  static constexpr int kLanes = G / kEPL;
   static constexpr int kGroupsPerWave = 64 / kLanes;
 };
 
-template <int BITS, int OUT_T, int CH, bool NT, bool NTP>
+template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
 __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32_t groups,
                                                              uint64_t seg_len, void* __restrict__ out) {
-  using M = GatherMap<OUT_T>;
+  using M = GatherMap<OUT_T, G>;
   constexpr int EPL = M::kEPL;
   const int p = blockIdx.y;
   const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(in.codes[p]);
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32
   for (int ch = 0; ch < CH; ++ch) {
     const uint32_t g = g0 + ch * M::kGroupsPerWave + lane / M::kLanes;
     if (g >= groups) break;   // lanes are independent here
-    const uint64_t k = (uint64_t)g * kGroup + (lane % M::kLanes) * EPL;
+    const uint64_t k = (uint64_t)g * G + (lane % M::kLanes) * EPL;
     const uint32_t pw = params[g];
     const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
     float d[EPL];
@@ -482,76 +483,84 @@ unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned grid_x)
 
 }  // namespace
 
-template <int BITS, int IN_T, int ST_T, bool NT, bool XCD>
+template <int BITS, int IN_T, int ST_T, int G, bool NT, bool XCD>
 void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
-  const uint64_t groups = a.seg_len / kGroup;
+  const uint64_t groups = a.seg_len / G;
   const unsigned ny = (unsigned)(a.P - 1);
-  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, grid_x), ny);
-  hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, NT, XCD>), grid, dim3(kThreads), 0, st,
-                     static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
+  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock, grid_x), ny);
+  hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, G, NT, XCD>), grid, dim3(kThreads), 0,
+                     st, static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
                      (uint32_t)groups, a.seg_len, a.coef);
 }
 
-template <int BITS, int IN_T, int ST_T, int OUT_T, bool NT, bool NTP, bool XCD>
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool XCD>
 void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
-  const uint64_t groups = a.seg_len / kGroup;
-  dim3 grid(blocks_for(groups, GroupMap<ST_T>::kGroupsPerBlock, grid_x));
-  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, NT, NTP, XCD>), grid,
+  const uint64_t groups = a.seg_len / G;
+  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock, grid_x));
+  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NT, NTP, XCD>), grid,
                      dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, a.segs,
                      a.P, a.rank, (uint32_t)groups, a.seg_len,
                      static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
 }
 
-template <int BITS, int OUT_T, int CH, bool NT, bool NTP>
+template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
 void launch_k3(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
-  const uint64_t groups = a.seg_len / kGroup;
-  constexpr int gpb = (kThreads / 64) * GatherMap<OUT_T>::kGroupsPerWave * CH;
+  const uint64_t groups = a.seg_len / G;
+  constexpr int gpb = (kThreads / 64) * GatherMap<OUT_T, G>::kGroupsPerWave * CH;
   dim3 grid(blocks_for(groups, gpb, grid_x), (unsigned)a.P);
-  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, CH, NT, NTP>), grid, dim3(kThreads), 0, st, a.segs,
-                     (uint32_t)groups, a.seg_len, a.out);
+  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>), grid, dim3(kThreads), 0, st,
+                     a.segs, (uint32_t)groups, a.seg_len, a.out);
 }
 
-// Nontemporal loads and stores for every streamed array; chunks per lane of
-// the gather pass.
-// The owner pass reads its P-1 incoming payloads with ordinary loads: the two
-// halves of a 128-byte code line belong to neighbouring waves of one block,
-// and a nontemporal first read makes the second fetch the line again.
+// Nontemporal loads and stores for every streamed array, except the owner
+// pass's incoming payloads: the two halves of a 128-byte code line belong to
+// neighbouring waves of one block, and a nontemporal first read makes the
+// second fetch the line again.
 constexpr bool kNT = true;
 constexpr bool kNTOwnerPayload = false;
 // XCD-contiguous block order: the owner pass reads P-1 parameter arrays at 4
 // bytes per group and gains from it; the entry pass measured slightly slower.
 constexpr bool kXcdOrderEntry = false, kXcdOrderOwner = true;
+// Chunks per lane of the gather pass.
 constexpr int kGatherChunks = 2;
 
-// Runtime -> template dispatch.
+// Runtime -> template dispatch: each call hands f one std::integral_constant.
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <typename F>
+void with_bits(int v, F&& f) { if (v == 4) f(IC<4>{}); else f(IC<8>{}); }
+template <typename F>
+void with_group(int v, F&& f) {
+  if (v == 32) f(IC<32>{});
+  else if (v == 64) f(IC<64>{});
+  else f(IC<128>{});
+}
+template <typename F>
+void with_in(int v, F&& f) { if (v == kInF16) f(IC<kInF16>{}); else f(IC<kInBF16>{}); }
+template <typename F>
+void with_state(int v, F&& f) { if (v == kStateBF16) f(IC<kStateBF16>{}); else f(IC<kStateF32>{}); }
+template <typename F>
+void with_out(int v, F&& f) { if (v == kOutF32) f(IC<kOutF32>{}); else f(IC<kOutBF16>{}); }
+
 void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
-#define ECHO_K1(B, I, S) \
-  if (a.bits == B && a.in_dtype == I && a.state_dtype == S) return launch_k1<B, I, S, kNT, kXcdOrderEntry>(a, 0, st);
-  ECHO_K1(4, kInBF16, kStateF32) ECHO_K1(4, kInBF16, kStateBF16)
-  ECHO_K1(4, kInF16, kStateF32)  ECHO_K1(4, kInF16, kStateBF16)
-  ECHO_K1(8, kInBF16, kStateF32) ECHO_K1(8, kInBF16, kStateBF16)
-  ECHO_K1(8, kInF16, kStateF32)  ECHO_K1(8, kInF16, kStateBF16)
-#undef ECHO_K1
+  with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
+    with_state(a.state_dtype, [&](auto S) {
+      launch_k1<B(), I(), S(), G(), kNT, kXcdOrderEntry>(a, 0, st);
+    }); }); }); });
 }
 
 void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
-#define ECHO_K2(B, I, S, O)                                                      \
-  if (a.bits == B && a.in_dtype == I && a.state_dtype == S && a.out_dtype == O) \
-    return launch_k2<B, I, S, O, kNT, kNTOwnerPayload, kXcdOrderOwner>(a, 0, st);
-#define ECHO_K2_IO(B, I) \
-  ECHO_K2(B, I, kStateF32, kOutBF16) ECHO_K2(B, I, kStateF32, kOutF32) \
-  ECHO_K2(B, I, kStateBF16, kOutBF16) ECHO_K2(B, I, kStateBF16, kOutF32)
-  ECHO_K2_IO(4, kInBF16) ECHO_K2_IO(4, kInF16) ECHO_K2_IO(8, kInBF16) ECHO_K2_IO(8, kInF16)
-#undef ECHO_K2_IO
-#undef ECHO_K2
+  with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
+    with_state(a.state_dtype, [&](auto S) { with_out(a.out_dtype, [&](auto O) {
+      launch_k2<B(), I(), S(), O(), G(), kNT, kNTOwnerPayload, kXcdOrderOwner>(a, 0, st);
+    }); }); }); }); });
 }
 
 void run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
-  constexpr int C = kGatherChunks;
-  if (a.bits == 4 && a.out_dtype == kOutBF16) return launch_k3<4, kOutBF16, C, kNT, kNT>(a, 0, st);
-  if (a.bits == 4 && a.out_dtype == kOutF32) return launch_k3<4, kOutF32, C, kNT, kNT>(a, 0, st);
-  if (a.bits == 8 && a.out_dtype == kOutBF16) return launch_k3<8, kOutBF16, C, kNT, kNT>(a, 0, st);
-  if (a.bits == 8 && a.out_dtype == kOutF32) return launch_k3<8, kOutF32, C, kNT, kNT>(a, 0, st);
+  with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_out(a.out_dtype, [&](auto O) {
+    launch_k3<B(), O(), G(), kGatherChunks, kNT, kNT>(a, 0, st);
+  }); }); });
 }
 
 void run_zero(void* p, uint64_t bytes, hipStream_t st) {

@@ -45,9 +45,9 @@ def alloc_ranks(cfg: B.echo_config, P: int, n: int, device, bits_max: int | None
     seg = n // P
     sdt = state_torch_dtype(cfg)
     state = [torch.empty(2 * n, dtype=sdt, device=device) for _ in range(P)]
-    sent = [[None if o == p else B.alloc_payload(seg, bits, device) for o in range(P)]
-            for p in range(P)]
-    owned = [B.alloc_payload(seg, bits, device) for _ in range(P)]
+    sent = [[None if o == p else B.alloc_payload(seg, bits, device, group=cfg.group)
+             for o in range(P)] for p in range(P)]
+    owned = [B.alloc_payload(seg, bits, device, group=cfg.group) for _ in range(P)]
     out = torch.empty(n, dtype=out_torch_dtype(cfg), device=device)
     r = Ranks(P, n, state, sent, owned, out)
     for p in range(P):

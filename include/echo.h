@@ -24,8 +24,9 @@
  * Layout (every call):
  *   - A message of n elements per rank is split into P equal contiguous
  *     segments; rank p owns segment p = [p*n/P, (p+1)*n/P).
- *   - Groups of 128 consecutive elements of a segment share one scale and
- *     one zero point, both IEEE binary16; params[g] = scale | zero << 16.
+ *   - Groups of `group` consecutive elements of a segment (128 by default;
+ *     32 and 64 are also accepted) share one scale and one zero point, both
+ *     IEEE binary16; params[g] = scale | zero << 16.
  *   - Codes: bits = 4 -> two per byte, the even element in the low nibble;
  *     bits = 8 -> one per byte.  Codes and params of a segment are two
  *     separate arrays ("payload", echo_seg).
@@ -75,11 +76,11 @@ extern "C" {
 #define ECHO_STATE_BF16  1   /*                   bfloat16 (round to nearest even) */
 
 #define ECHO_MAX_RANKS  16
-#define ECHO_GROUP      128  /* the only group size the GPU path accepts */
+#define ECHO_GROUP      128  /* default group size; 32 and 64 are also accepted */
 
 typedef struct echo_config {
     int32_t bits;        /* 4 or 8: code width ([JP-F]; 8-bit for early sites) */
-    int32_t group;       /* elements per scale/zero pair; must be ECHO_GROUP */
+    int32_t group;       /* elements per scale/zero pair: 32, 64 or 128 */
     int32_t in_dtype;    /* ECHO_IN_*    */
     int32_t out_dtype;   /* ECHO_OUT_*   */
     int32_t state_dtype; /* ECHO_STATE_* */
@@ -110,7 +111,7 @@ int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* strea
  * echo_quantize_feedback -- entry pass of rank `rank` ([JP-1], [JP-2]).
  *   For every element j of every segment p != rank:
  *     v = x[j] + eta * (S_j + L_j)                   (fp32, unfused)
- *   each 128-group of v is quantized to `bits` with an fp16 zero point
+ *   each group of v is quantized to `bits` with an fp16 zero point
  *   (the group minimum) and fp16 step ((max - zero) / (2^bits - 1)), codes
  *   round half to even; the payload goes to out[p].  With r = v - dequant:
  *     S_j = beta_short * S_j + (1-beta_short)(1-mix_long) * r
@@ -135,7 +136,7 @@ int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n,
  *     v_own = x[j] + eta * (S_j + L_j)
  *     acc   = sum over p = 0..P-1 in that order of
  *             (p == rank ? v_own : dequant of in[p]'s code for j)    (fp32)
- *   acc is requantized per 128-group into *out (same quantizer as above);
+ *   acc is requantized per group into *out (same quantizer as above);
  *   o = the output value of j (bf16-rounded dequant for ECHO_OUT_BF16,
  *   the fp32 dequant for ECHO_OUT_F32); r = acc - o; S_j and L_j are
  *   updated with r as above.  Segments p != rank of x and state are not

@@ -78,11 +78,11 @@ def state_as_f32(a: np.ndarray) -> np.ndarray:
     return a
 
 
-def random_payload_host(rng, seg: int, bits: int):
+def random_payload_host(rng, seg: int, bits: int, group: int = G):
     """Arbitrary codes and finite fp16 scale/zero pairs (including subnormal
     and zero scales) as incoming payload test data."""
     codes = rng.integers(0, 256, size=seg * bits // 8, dtype=np.uint8)
-    ng = seg // G
+    ng = seg // group
     sb = rng.integers(0, 0x7800, size=ng).astype(np.uint32)        # finite, |s| < 32768
     sb[rng.random(ng) < 0.05] = 0
     sb[rng.random(ng) < 0.05] = rng.integers(1, 0x400)              # subnormal steps

@@ -72,7 +72,9 @@ def cfg(**kw):
 @pytest.mark.parametrize("call,code", [
     (lambda L: L.echo_quantize_feedback(None, 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(cfg(bits=3), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
-    (lambda L: L.echo_quantize_feedback(cfg(group=64), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(group=48), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(group=256), 2, 0, 512, A, A, SEGS, None), B.ECHO_ERR_ARG),
+    (lambda L: L.echo_quantize_feedback(cfg(group=64), 2, 0, 192, A, A, SEGS, None), B.ECHO_ERR_SHAPE),
     (lambda L: L.echo_quantize_feedback(cfg(in_dtype=7), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(cfg(eta=float("nan")), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(cfg(beta_short=1.0), 2, 0, 256, A, A, SEGS, None), B.ECHO_ERR_ARG),

@@ -73,23 +73,24 @@ def cmp_state(gpu_state, S_ref, L_ref, what):
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("in_dtype,state_dtype", TYPES)
 @pytest.mark.parametrize("P,groups", [(2, 37), (3, 8), (4, 1), (8, 21), (16, 3)])
-def test_entry_pass(P, groups, bits, in_dtype, state_dtype):
-    banner(f"entry P={P} groups={groups} bits={bits} in={in_dtype} state={state_dtype}")
-    rng = np.random.default_rng(1000 * P + groups + bits)
-    seg = groups * G
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_entry_pass(P, groups, bits, in_dtype, state_dtype, group):
+    banner(f"entry P={P} groups={groups} bits={bits} in={in_dtype} state={state_dtype} group={group}")
+    rng = np.random.default_rng(1000 * P + groups + bits + group)
+    seg = groups * group
     n = P * seg
-    cfg = B.make_config(bits=bits, in_dtype=in_dtype, state_dtype=state_dtype)
+    cfg = B.make_config(bits=bits, group=group, in_dtype=in_dtype, state_dtype=state_dtype)
     ocfg = oracle_config(cfg)
     for rank in sorted({0, P - 1, P // 2}):
         xb, tdt = rand_input(rng, n, in_dtype, special=(rank == 0))
         s0, l0 = rand_state(rng, n, state_dtype), rand_state(rng, n, state_dtype, 0.2)
         x = device_bits16(xb, tdt, DEV)
         state = state_dev(interleave(s0, l0))
-        out = [B.alloc_payload(seg, bits, DEV, fill=0xA5) for _ in range(P)]
+        out = [B.alloc_payload(seg, bits, DEV, fill=0xA5, group=group) for _ in range(P)]
         B.echo_quantize_feedback(cfg, P, rank, n, x, state, out)
         torch.cuda.synchronize()
         oc = [np.zeros(seg * bits // 8, np.uint8) if p != rank else None for p in range(P)]
-        op = [np.zeros(groups, np.uint32) if p != rank else None for p in range(P)]
+        op = [np.zeros(groups, np.uint32) if p != rank else None for p in range(P)]   # groups per segment
         so, lo = s0.copy(), l0.copy()
         O.quantize_feedback(ocfg, P, rank, xb, so, lo, oc, op)
         for p in range(P):
@@ -111,17 +112,20 @@ def test_entry_pass(P, groups, bits, in_dtype, state_dtype):
 @pytest.mark.parametrize("out_dtype", [B.ECHO_OUT_BF16, B.ECHO_OUT_F32])
 @pytest.mark.parametrize("in_dtype,state_dtype", TYPES)
 @pytest.mark.parametrize("P,groups", [(1, 9), (2, 37), (5, 8), (8, 13), (16, 2)])
-def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype):
-    banner(f"owner P={P} groups={groups} bits={bits} out={out_dtype} in={in_dtype} state={state_dtype}")
-    rng = np.random.default_rng(2000 * P + groups + bits + 10 * out_dtype)
-    seg = groups * G
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype, group):
+    banner(f"owner P={P} groups={groups} bits={bits} out={out_dtype} in={in_dtype} "
+           f"state={state_dtype} group={group}")
+    rng = np.random.default_rng(2000 * P + groups + bits + 10 * out_dtype + group)
+    seg = groups * group
     n = P * seg
-    cfg = B.make_config(bits=bits, in_dtype=in_dtype, out_dtype=out_dtype, state_dtype=state_dtype)
+    cfg = B.make_config(bits=bits, group=group, in_dtype=in_dtype, out_dtype=out_dtype,
+                        state_dtype=state_dtype)
     ocfg = oracle_config(cfg)
     for rank in sorted({0, P - 1}):
         xb, tdt = rand_input(rng, n, in_dtype, special=(rank == 0))
         s0, l0 = rand_state(rng, n, state_dtype), rand_state(rng, n, state_dtype, 0.2)
-        inc = [None if p == rank else random_payload_host(rng, seg, bits) for p in range(P)]
+        inc = [None if p == rank else random_payload_host(rng, seg, bits, group) for p in range(P)]
         if rank == 0 and P > 1:    # one sender of exactly representable integers
             k = rng.integers(0, 1 << bits, size=seg)
             c = k.astype(np.uint8) if bits == 8 else (k[0::2] | (k[1::2] << 4)).astype(np.uint8)
@@ -129,7 +133,7 @@ def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype):
         x = device_bits16(xb, tdt, DEV)
         state = state_dev(interleave(s0, l0))
         inp = [None if pl is None else to_device_payload(pl[0], pl[1], DEV) for pl in inc]
-        out = B.alloc_payload(seg, bits, DEV, fill=0x5A)
+        out = B.alloc_payload(seg, bits, DEV, fill=0x5A, group=group)
         B.echo_owner_reduce_requant(cfg, P, rank, n, x, state, inp, out)
         torch.cuda.synchronize()
         oc = np.zeros(seg * bits // 8, np.uint8)
@@ -151,14 +155,15 @@ def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype):
 # ------------------------------------------------------------------ dequantize
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("out_dtype", [B.ECHO_OUT_BF16, B.ECHO_OUT_F32])
-@pytest.mark.parametrize("P,groups", [(1, 5), (2, 37), (8, 17), (16, 1)])
-def test_dequant_gather(P, groups, bits, out_dtype):
-    banner(f"gather P={P} groups={groups} bits={bits} out={out_dtype}")
-    rng = np.random.default_rng(3000 * P + groups + bits + out_dtype)
-    seg = groups * G
+@pytest.mark.parametrize("P,groups", [(1, 5), (2, 37), (8, 17), (16, 1), (3, 123)])
+@pytest.mark.parametrize("group", [128, 64, 32])
+def test_dequant_gather(P, groups, bits, out_dtype, group):
+    banner(f"gather P={P} groups={groups} bits={bits} out={out_dtype} group={group}")
+    rng = np.random.default_rng(3000 * P + groups + bits + out_dtype + group)
+    seg = groups * group
     n = P * seg
-    cfg = B.make_config(bits=bits, out_dtype=out_dtype)
-    pls = [random_payload_host(rng, seg, bits) for _ in range(P)]
+    cfg = B.make_config(bits=bits, group=group, out_dtype=out_dtype)
+    pls = [random_payload_host(rng, seg, bits, group) for _ in range(P)]
     inp = [to_device_payload(c, q, DEV) for c, q in pls]
     odt = torch.bfloat16 if out_dtype == B.ECHO_OUT_BF16 else torch.float32
     out = torch.empty(n + 64, dtype=odt, device=DEV)
@@ -187,21 +192,25 @@ def test_state_reset(n, state_dtype):
 
 
 # ------------------------------------------------------------------ whole call
-@pytest.mark.parametrize("P,groups,bits,out_dtype,state_dtype", [
-    (1, 16, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_F32),
-    (2, 1024, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_F32),     # the single-call 256k message
-    (4, 77, 8, B.ECHO_OUT_F32, B.ECHO_STATE_F32),
-    (8, 29, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_BF16),
-    (16, 5, 4, B.ECHO_OUT_F32, B.ECHO_STATE_BF16),
+@pytest.mark.parametrize("P,groups,bits,out_dtype,state_dtype,group", [
+    (1, 16, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_F32, 128),
+    (2, 1024, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_F32, 128),     # the single-call 256k message
+    (4, 77, 8, B.ECHO_OUT_F32, B.ECHO_STATE_F32, 128),
+    (8, 29, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_BF16, 128),
+    (16, 5, 4, B.ECHO_OUT_F32, B.ECHO_STATE_BF16, 128),
+    (4, 61, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_F32, 64),
+    (8, 45, 8, B.ECHO_OUT_BF16, B.ECHO_STATE_BF16, 64),
+    (4, 99, 4, B.ECHO_OUT_BF16, B.ECHO_STATE_F32, 32),
+    (8, 33, 4, B.ECHO_OUT_F32, B.ECHO_STATE_BF16, 32),
 ])
-def test_allreduce_three_calls(P, groups, bits, out_dtype, state_dtype):
+def test_allreduce_three_calls(P, groups, bits, out_dtype, state_dtype, group):
     """Three chained calls over P simulated ranks, state carried: every
     payload, the output and every rank's state against the oracle."""
-    banner(f"allreduce P={P} groups={groups} bits={bits}")
-    rng = np.random.default_rng(4000 + P + groups)
-    seg = groups * G
+    banner(f"allreduce P={P} groups={groups} bits={bits} group={group}")
+    rng = np.random.default_rng(4000 + P + groups + group)
+    seg = groups * group
     n = P * seg
-    cfg = B.make_config(bits=bits, out_dtype=out_dtype, state_dtype=state_dtype)
+    cfg = B.make_config(bits=bits, group=group, out_dtype=out_dtype, state_dtype=state_dtype)
     ocfg = oracle_config(cfg)
     r = sim.alloc_ranks(cfg, P, n, DEV)
     oS = [np.zeros(n, O.state_np_dtype(ocfg)) for _ in range(P)]
