@@ -24,8 +24,8 @@ ECHO_MAX_RANKS = 16
 ECHO_GROUP = 128
 
 EXPORTED = ("echo_state_reset", "echo_quantize_feedback", "echo_owner_reduce_requant",
-            "echo_dequant_gather", "echo_codes_bytes", "echo_params_bytes", "echo_state_bytes",
-            "echo_error_string")
+            "echo_dequant_gather", "echo_segment_len", "echo_codes_bytes", "echo_params_bytes",
+            "echo_state_bytes", "echo_error_string")
 
 
 class echo_config(ctypes.Structure):
@@ -66,6 +66,8 @@ def load_library() -> ctypes.CDLL:
         L.echo_codes_bytes.argtypes = [i64, i32]
         L.echo_params_bytes.argtypes = [i64, i32]
         L.echo_state_bytes.argtypes = [i64, i32]
+        L.echo_segment_len.argtypes = [i64, i32, i32]
+        L.echo_segment_len.restype = ctypes.c_int64
         L.echo_codes_bytes.restype = ctypes.c_size_t
         L.echo_params_bytes.restype = ctypes.c_size_t
         L.echo_state_bytes.restype = ctypes.c_size_t
@@ -105,6 +107,10 @@ def echo_codes_bytes(seg_len: int, bits: int) -> int:
 
 def echo_params_bytes(seg_len: int, group: int = ECHO_GROUP) -> int:
     return load_library().echo_params_bytes(seg_len, group)
+
+
+def echo_segment_len(n: int, P: int, group: int = ECHO_GROUP) -> int:
+    return load_library().echo_segment_len(n, P, group)
 
 
 def echo_state_bytes(n: int, state_dtype: int) -> int:

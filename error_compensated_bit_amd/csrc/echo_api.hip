@@ -28,14 +28,18 @@ int check_config(const echo_config* c) {
   return ECHO_OK;
 }
 
-// P ranks, message of n elements: n must be a positive multiple of P*group,
-// and a segment may hold at most 2^31 groups (the kernels' 32-bit group
-// index then cannot wrap).
+// Segments of whole groups: ceil(n/P) rounded up to a multiple of the group.
+int64_t segment_len(int64_t n, int P, int group) {
+  const int64_t per = (n + P - 1) / P;
+  return (per + group - 1) / group * group;
+}
+
+// P ranks, message of n >= 1 elements; a segment may hold at most 2^31 groups
+// (the kernels' 32-bit group index then cannot wrap).
 int check_shape(int P, int64_t n, int group) {
   if (P < 1 || P > ECHO_MAX_RANKS) return ECHO_ERR_ARG;
   if (n <= 0) return ECHO_ERR_SHAPE;
-  if (n % ((int64_t)P * group) != 0) return ECHO_ERR_SHAPE;
-  if (n / P / group > ((int64_t)1 << 31)) return ECHO_ERR_SHAPE;
+  if (segment_len(n, P, group) / group > ((int64_t)1 << 31)) return ECHO_ERR_SHAPE;
   return ECHO_OK;
 }
 
@@ -73,7 +77,8 @@ LaunchArgs base_args(const echo_config* c, int P, int rank, int64_t n) {
   a.state_dtype = c->state_dtype;
   a.P = P;
   a.rank = rank;
-  a.seg_len = (uint64_t)(n / P);
+  a.n = (uint64_t)n;
+  a.seg_len = (uint64_t)segment_len(n, P, c->group);
   a.coef = make_coef(c);
   return a;
 }
@@ -164,6 +169,11 @@ size_t echo_codes_bytes(int64_t seg_len, int bits) {
   return (size_t)seg_len * (size_t)bits / 8;
 }
 
+int64_t echo_segment_len(int64_t n, int P, int group) {
+  if (n <= 0 || P < 1 || P > ECHO_MAX_RANKS || (group != 32 && group != 64 && group != 128)) return 0;
+  return segment_len(n, P, group);
+}
+
 size_t echo_state_bytes(int64_t n, int state_dtype) {
   if (n <= 0) return 0;
   if (state_dtype == ECHO_STATE_F32) return (size_t)n * 8;
@@ -180,7 +190,7 @@ const char* echo_error_string(int code) {
   switch (code) {
     case ECHO_OK: return "ok";
     case ECHO_ERR_ARG: return "invalid argument";
-    case ECHO_ERR_SHAPE: return "message length is not a positive multiple of P * group";
+    case ECHO_ERR_SHAPE: return "message length is not positive or a segment exceeds 2^31 groups";
     case ECHO_ERR_ALIGN: return "buffer not 16-byte aligned";
     case ECHO_ERR_HIP: return "HIP launch error";
     default: return "unknown error";

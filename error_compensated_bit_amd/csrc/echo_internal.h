@@ -32,7 +32,8 @@ struct Coef {
 struct LaunchArgs {
   int bits, group, in_dtype, out_dtype, state_dtype;
   int P, rank;
-  uint64_t seg_len;
+  uint64_t n;         // elements of the message
+  uint64_t seg_len;   // elements per segment: ceil(ceil(n/P)/group)*group
   const void* x;
   void* state;   // interleaved short/long memories: state[2j] = S_j, state[2j+1] = L_j
   SegTable segs;

@@ -203,6 +203,84 @@ struct CodeIO {
   }
 };
 
+// Element-wise forms for the one partial group of a ragged message: only the
+// lane's first nv elements exist (nv = 0 .. EPL); nothing past them is read
+// or written.  An INT4 byte holding one valid element gets a 0 high nibble.
+template <int IN_T, int EPL>
+__device__ __forceinline__ void load_in_part(const uint16_t* __restrict__ p, float* v, int nv) {
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) v[i] = i < nv ? in_to_f32<IN_T>(p[i]) : 0.0f;
+}
+
+template <int ST_T>
+__device__ __forceinline__ void load_state_part(const void* base, uint64_t e, float* s, float* l,
+                                                int nv) {
+#pragma unroll
+  for (int i = 0; i < StateIO<ST_T>::kEPL; ++i) {
+    s[i] = l[i] = 0.0f;
+    if (i < nv) {
+      if constexpr (ST_T == kStateF32) {
+        const float* q = static_cast<const float*>(base) + 2 * (e + i);
+        s[i] = q[0];
+        l[i] = q[1];
+      } else {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + 2 * (e + i));
+        s[i] = bf16_to_f32(w & 0xffffu);
+        l[i] = bf16_to_f32(w >> 16);
+      }
+    }
+  }
+}
+
+template <int ST_T>
+__device__ __forceinline__ void store_state_part(void* base, uint64_t e, const float* s,
+                                                 const float* l, int nv) {
+#pragma unroll
+  for (int i = 0; i < StateIO<ST_T>::kEPL; ++i) {
+    if (i < nv) {
+      if constexpr (ST_T == kStateF32) {
+        float* q = static_cast<float*>(base) + 2 * (e + i);
+        q[0] = s[i];
+        q[1] = l[i];
+      } else {
+        *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + 2 * (e + i)) =
+            f32_to_bf16(s[i]) | (f32_to_bf16(l[i]) << 16);
+      }
+    }
+  }
+}
+
+template <int BITS, int EPL>
+__device__ __forceinline__ void store_codes_part(uint8_t* __restrict__ codes, uint64_t k,
+                                                 const uint32_t* q, int nv) {
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (i < nv) codes[k + i] = (uint8_t)q[i];
+  } else {
+#pragma unroll
+    for (int b = 0; b < EPL / 2; ++b)
+      if (2 * b < nv) codes[k / 2 + b] = (uint8_t)(q[2 * b] | ((2 * b + 1 < nv ? q[2 * b + 1] : 0u) << 4));
+  }
+}
+
+// Full groups per segment: `all` in segments before `last` (the last
+// non-empty one), `in_last` in it, none after it.
+struct FullGroups {
+  uint32_t all, last, in_last;
+  __device__ __forceinline__ uint32_t of(uint32_t p) const {
+    return p < last ? all : (p == last ? in_last : 0u);
+  }
+};
+
+// Elements of segment p of a message of n elements cut into segments of
+// seg_len: seg_len everywhere but the last non-empty segment, 0 after it.
+__device__ __forceinline__ uint64_t segment_count(uint64_t n, uint64_t seg_len, uint32_t p) {
+  const uint64_t start = (uint64_t)p * seg_len;
+  if (start >= n) return 0;
+  return (n - start) < seg_len ? (n - start) : seg_len;
+}
+
 template <int BITS>
 __device__ __forceinline__ uint32_t code_at(uint32_t word, int i) {
   return BITS == 4 ? (word >> (4 * i)) & 0xfu : (word >> (8 * i)) & 0xffu;
@@ -273,124 +351,195 @@ __device__ __forceinline__ void group_minmax(float& mn, float& mx) {
 // ------------------------------------------------------------------ K1
 // Entry pass of `rank` ([JP-1]: only the segments this rank does not own are
 // quantized; [JP-2]: feedback-add, residual and state update fused here).
-// grid.y = P-1 non-owned segments, grid.x covers the segment's groups, one
-// group per run of G/EPL lanes.
+// One group of G elements per run of G/EPL lanes.  FULL: every element of
+// the group exists; otherwise the lane holds nv of its EPL elements.
+template <int BITS, int IN_T, int ST_T, int G, bool NT, bool FULL>
+__device__ __forceinline__ void entry_group(const uint16_t* __restrict__ x, void* __restrict__ state,
+                                            uint8_t* __restrict__ codes, uint32_t* __restrict__ params,
+                                            uint32_t g, uint32_t lane, uint64_t base, int nv,
+                                            const Coef& c) {
+  using M = GroupMap<ST_T, G>;
+  constexpr int E = M::kEPL;
+  const uint64_t k = (uint64_t)g * G + lane * E;   // index within the segment
+  const uint64_t e = base + k;
+  float xv[E], s[E], l[E], v[E];
+  if constexpr (FULL) {
+    load_in<IN_T, E, NT>(x + e, xv);
+    StateIO<ST_T>::template load<NT>(state, e, s, l);
+  } else {
+    load_in_part<IN_T, E>(x + e, xv, nv);
+    load_state_part<ST_T>(state, e, s, l, nv);
+  }
+  float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    v[i] = feedback(xv[i], s[i], l[i], c.eta);
+    if (FULL || i < nv) {
+      mn = fminf(mn, v[i]);
+      mx = fmaxf(mx, v[i]);
+    }
+  }
+  group_minmax<M::kLanes>(mn, mx);
+  const QParams qp = group_params<BITS>(mn, mx);
+  uint32_t q[E];
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    q[i] = (FULL || i < nv) ? encode<BITS>(v[i], qp) : 0u;
+    ema(s[i], l[i], v[i] - decode(q[i], qp.sf, qp.zf), c);
+  }
+  if constexpr (FULL) {
+    StateIO<ST_T>::template store<NT>(state, e, s, l);
+    CodeIO<BITS, E>::template store<NT>(codes, k, q);
+  } else {
+    store_state_part<ST_T>(state, e, s, l, nv);
+    store_codes_part<BITS, E>(codes, k, q, nv);
+  }
+  if (lane == 0) params[g] = qp.word;
+}
+
+// grid.y = P-1 non-owned segments, grid.x covers a full segment's groups.
+// Full groups only; the partial group of a ragged message goes to
+// k_quant_feedback_tail, so this kernel carries no guarded path.
 template <int BITS, int IN_T, int ST_T, int G, bool NT, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_quant_feedback(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable out, int rank,
-    uint32_t groups, uint64_t seg_len, Coef c) {
+    FullGroups fg, uint64_t seg_len, Coef c) {
   using M = GroupMap<ST_T, G>;
-  constexpr int E = M::kEPL;
   uint32_t bx = blockIdx.x, slot = blockIdx.y;
   if constexpr (XCD) {
     const uint32_t L = xcd_contiguous_block(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
     slot = L / gridDim.x;
     bx = L - slot * gridDim.x;
   }
-  const int p = (int)slot + ((int)slot >= rank ? 1 : 0);
-  const uint64_t base = (uint64_t)p * seg_len;
-  uint8_t* __restrict__ codes = static_cast<uint8_t*>(out.codes[p]);
-  uint32_t* __restrict__ params = out.params[p];
+  const uint32_t p = slot + ((int)slot >= rank ? 1u : 0u);
   const uint32_t lane = threadIdx.x % M::kLanes;
   const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
-  if (g >= groups) return;   // whole groups only: the lanes of a group leave together
-  {
-    const uint64_t k = (uint64_t)g * G + lane * E;   // index within the segment
-    const uint64_t e = base + k;
-    float xv[E], s[E], l[E], v[E];
-    load_in<IN_T, E, NT>(x + e, xv);
-    StateIO<ST_T>::template load<NT>(state, e, s, l);
-    float mn = INFINITY, mx = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      v[i] = feedback(xv[i], s[i], l[i], c.eta);
-      mn = fminf(mn, v[i]);
-      mx = fmaxf(mx, v[i]);
-    }
-    group_minmax<M::kLanes>(mn, mx);
-    const QParams qp = group_params<BITS>(mn, mx);
-    uint32_t q[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) {
-      q[i] = encode<BITS>(v[i], qp);
-      ema(s[i], l[i], v[i] - decode(q[i], qp.sf, qp.zf), c);
-    }
-    StateIO<ST_T>::template store<NT>(state, e, s, l);
-    CodeIO<BITS, E>::template store<NT>(codes, k, q);
-    if (lane == 0) params[g] = qp.word;
-  }
+  if (g >= fg.of(p)) return;   // whole groups only: the lanes of a group leave together
+  entry_group<BITS, IN_T, ST_T, G, NT, true>(x, state, static_cast<uint8_t*>(out.codes[p]),
+                                             out.params[p], g, lane, (uint64_t)p * seg_len,
+                                             M::kEPL, c);
+}
+
+// The one partial group (`valid` < G elements) of segment p: one block of
+// G/EPL lanes.
+template <int BITS, int IN_T, int ST_T, int G>
+__global__ void k_quant_feedback_tail(const uint16_t* __restrict__ x, void* __restrict__ state,
+                                      uint8_t* __restrict__ codes, uint32_t* __restrict__ params,
+                                      uint64_t base, uint32_t g, uint32_t valid, Coef c) {
+  using M = GroupMap<ST_T, G>;
+  const int nv = (int)valid - (int)threadIdx.x * M::kEPL;
+  entry_group<BITS, IN_T, ST_T, G, false, false>(x, state, codes, params, g, threadIdx.x, base,
+                                                 nv < 0 ? 0 : nv > M::kEPL ? M::kEPL : nv, c);
 }
 
 // ------------------------------------------------------------------ K2
 // Owner pass over segment `rank` ([JP-1]: sum in fp32 in rank order with the
 // owner's own unquantized term, requantize; [JP-W] the round trip; [JP-2]
 // the owner's residual against the output value, state update fused).
-template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool XCD>
-__global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
-    const uint16_t* __restrict__ x, void* __restrict__ state, SegTable in, int P, int rank,
-    uint32_t groups, uint64_t seg_len, uint8_t* __restrict__ out_codes,
-    uint32_t* __restrict__ out_params, Coef c) {
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool FULL>
+__device__ __forceinline__ void owner_group(const uint16_t* __restrict__ x, void* __restrict__ state,
+                                            const SegTable& in, int P, int rank,
+                                            uint8_t* __restrict__ out_codes,
+                                            uint32_t* __restrict__ out_params, uint32_t g,
+                                            uint32_t lane, uint64_t base, int nv, const Coef& c) {
   using M = GroupMap<ST_T, G>;
   constexpr int E = M::kEPL;
-  const uint64_t base = (uint64_t)rank * seg_len;
-  const uint32_t lane = threadIdx.x % M::kLanes;
-  const uint32_t bx = XCD ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
-  const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
-  if (g >= groups) return;
-  {
-    const uint64_t k = (uint64_t)g * G + lane * E;
-    const uint64_t e = base + k;
-    // incoming payload words first, so that all loads are in flight together
-    uint32_t cw[kMaxRanks], pw[kMaxRanks];
+  const uint64_t k = (uint64_t)g * G + lane * E;
+  const uint64_t e = base + k;
+  // incoming payload words first, so that all loads are in flight together
+  // (a payload is sized for a full segment: the word of a partial group
+  // exists, its bytes past the group's end are ignored)
+  uint32_t cw[kMaxRanks], pw[kMaxRanks];
 #pragma unroll
-    for (int p = 0; p < kMaxRanks; ++p) {
-      if (p < P && p != rank) {
-        cw[p] = CodeIO<BITS, E>::template load<NTP>(static_cast<const uint8_t*>(in.codes[p]), k);
-        pw[p] = in.params[p][g];
-      }
+  for (int p = 0; p < kMaxRanks; ++p) {
+    if (p < P && p != rank) {
+      cw[p] = CodeIO<BITS, E>::template load<NTP>(static_cast<const uint8_t*>(in.codes[p]), k);
+      pw[p] = in.params[p][g];
     }
-    float xv[E], s[E], l[E], acc[E];
+  }
+  float xv[E], s[E], l[E], acc[E];
+  if constexpr (FULL) {
     load_in<IN_T, E, NT>(x + e, xv);
     StateIO<ST_T>::template load<NT>(state, e, s, l);
+  } else {
+    load_in_part<IN_T, E>(x + e, xv, nv);
+    load_state_part<ST_T>(state, e, s, l, nv);
+  }
 #pragma unroll
-    for (int p = 0; p < kMaxRanks; ++p) {
-      if (p < P) {
-        if (p == rank) {
+  for (int p = 0; p < kMaxRanks; ++p) {
+    if (p < P) {
+      if (p == rank) {
 #pragma unroll
-          for (int i = 0; i < E; ++i) {
-            const float t = feedback(xv[i], s[i], l[i], c.eta);
-            acc[i] = (p == 0) ? t : acc[i] + t;
-          }
-        } else {
-          const float sf = f16_to_f32(pw[p] & 0xffffu), zf = f16_to_f32(pw[p] >> 16);
+        for (int i = 0; i < E; ++i) {
+          const float t = feedback(xv[i], s[i], l[i], c.eta);
+          acc[i] = (p == 0) ? t : acc[i] + t;
+        }
+      } else {
+        const float sf = f16_to_f32(pw[p] & 0xffffu), zf = f16_to_f32(pw[p] >> 16);
 #pragma unroll
-          for (int i = 0; i < E; ++i) {
-            const float t = decode(code_at<BITS>(cw[p], i), sf, zf);
-            acc[i] = (p == 0) ? t : acc[i] + t;
-          }
+        for (int i = 0; i < E; ++i) {
+          const float t = decode(code_at<BITS>(cw[p], i), sf, zf);
+          acc[i] = (p == 0) ? t : acc[i] + t;
         }
       }
     }
-    float mn = INFINITY, mx = -INFINITY;
+  }
+  float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
+  for (int i = 0; i < E; ++i) {
+    if (FULL || i < nv) {
       mn = fminf(mn, acc[i]);
       mx = fmaxf(mx, acc[i]);
     }
-    group_minmax<M::kLanes>(mn, mx);
-    const QParams qp = group_params<BITS>(mn, mx);
-    uint32_t q[E];
+  }
+  group_minmax<M::kLanes>(mn, mx);
+  const QParams qp = group_params<BITS>(mn, mx);
+  uint32_t q[E];
 #pragma unroll
-    for (int i = 0; i < E; ++i) {
-      q[i] = encode<BITS>(acc[i], qp);
-      const float d = decode(q[i], qp.sf, qp.zf);
-      const float o = (OUT_T == kOutBF16) ? bf16_to_f32(f32_to_bf16(d)) : d;
-      ema(s[i], l[i], acc[i] - o, c);
-    }
+  for (int i = 0; i < E; ++i) {
+    q[i] = (FULL || i < nv) ? encode<BITS>(acc[i], qp) : 0u;
+    const float d = decode(q[i], qp.sf, qp.zf);
+    const float o = (OUT_T == kOutBF16) ? bf16_to_f32(f32_to_bf16(d)) : d;
+    ema(s[i], l[i], acc[i] - o, c);
+  }
+  if constexpr (FULL) {
     StateIO<ST_T>::template store<NT>(state, e, s, l);
     CodeIO<BITS, E>::template store<NT>(out_codes, k, q);
-    if (lane == 0) out_params[g] = qp.word;
+  } else {
+    store_state_part<ST_T>(state, e, s, l, nv);
+    store_codes_part<BITS, E>(out_codes, k, q, nv);
   }
+  if (lane == 0) out_params[g] = qp.word;
+}
+
+// Full groups only (see k_quant_feedback); the partial group goes to
+// k_owner_reduce_requant_tail.
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool XCD>
+__global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
+    const uint16_t* __restrict__ x, void* __restrict__ state, SegTable in, int P, int rank,
+    FullGroups fg, uint64_t seg_len, uint8_t* __restrict__ out_codes,
+    uint32_t* __restrict__ out_params, Coef c) {
+  using M = GroupMap<ST_T, G>;
+  const uint32_t lane = threadIdx.x % M::kLanes;
+  const uint32_t bx = XCD ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
+  const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
+  if (g >= fg.of((uint32_t)rank)) return;
+  owner_group<BITS, IN_T, ST_T, OUT_T, G, NT, NTP, true>(x, state, in, P, rank, out_codes,
+                                                         out_params, g, lane,
+                                                         (uint64_t)rank * seg_len, M::kEPL, c);
+}
+
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G>
+__global__ void k_owner_reduce_requant_tail(const uint16_t* __restrict__ x, void* __restrict__ state,
+                                            SegTable in, int P, int rank,
+                                            uint8_t* __restrict__ out_codes,
+                                            uint32_t* __restrict__ out_params, uint64_t base,
+                                            uint32_t g, uint32_t valid, Coef c) {
+  using M = GroupMap<ST_T, G>;
+  const int nv = (int)valid - (int)threadIdx.x * M::kEPL;
+  owner_group<BITS, IN_T, ST_T, OUT_T, G, false, false, false>(
+      x, state, in, P, rank, out_codes, out_params, g, threadIdx.x, base,
+      nv < 0 ? 0 : nv > M::kEPL ? M::kEPL : nv, c);
 }
 
 // ------------------------------------------------------------------ K3
@@ -407,11 +556,12 @@ struct GatherMap {
 };
 
 template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
-__global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32_t groups,
+__global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint64_t n,
                                                              uint64_t seg_len, void* __restrict__ out) {
   using M = GatherMap<OUT_T, G>;
   constexpr int EPL = M::kEPL;
   const int p = blockIdx.y;
+  const uint64_t len = segment_count(n, seg_len, (uint32_t)p);
   const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(in.codes[p]);
   const uint32_t* __restrict__ params = in.params[p];
   const uint64_t base = (uint64_t)p * seg_len;
@@ -420,8 +570,8 @@ __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) {
     const uint32_t g = g0 + ch * M::kGroupsPerWave + lane / M::kLanes;
-    if (g >= groups) break;   // lanes are independent here
     const uint64_t k = (uint64_t)g * G + (lane % M::kLanes) * EPL;
+    if (k >= len) break;   // lanes are independent here
     const uint32_t pw = params[g];
     const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
     float d[EPL];
@@ -445,7 +595,18 @@ __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint32
 #pragma unroll
       for (int i = 0; i < 4; ++i) d[i] = decode((w >> (8 * i)) & 0xffu, sf, zf);
     }
-    if constexpr (OUT_T == kOutBF16) {
+    if (k + EPL > len) {   // the last lane of a ragged message: element-wise stores
+      const int nv = (int)(len - k);
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        if (i < nv) {
+          if constexpr (OUT_T == kOutBF16)
+            static_cast<uint16_t*>(out)[base + k + i] = (uint16_t)f32_to_bf16(d[i]);
+          else
+            static_cast<float*>(out)[base + k + i] = d[i];
+        }
+      }
+    } else if constexpr (OUT_T == kOutBF16) {
       u32x4 o;
       o.x = f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16);
       o.y = f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16);
@@ -474,6 +635,22 @@ __global__ __launch_bounds__(kThreads) void k_zero(uint8_t* __restrict__ a, uint
 // ------------------------------------------------------------------ launchers
 namespace {
 
+// The partial group of a ragged message, if any: segment p, group g, and its
+// number of elements (valid = 0: every group is full).
+struct Tail {
+  uint32_t p, g, valid;
+};
+Tail tail_of(uint64_t n, uint64_t seg_len, int group) {
+  const uint64_t p = (n - 1) / seg_len;                 // last non-empty segment
+  const uint64_t len = n - p * seg_len;
+  return Tail{(uint32_t)p, (uint32_t)(len / group), (uint32_t)(len % group)};
+}
+
+FullGroups full_groups(uint64_t n, uint64_t seg_len, int group) {
+  const Tail t = tail_of(n, seg_len, group);
+  return FullGroups{(uint32_t)(seg_len / group), t.p, t.g};
+}
+
 // Blocks along x: `grid_x` when given, else one launch slot per group.
 unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned grid_x) {
   if (grid_x) return grid_x;
@@ -490,7 +667,13 @@ void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock, grid_x), ny);
   hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, G, NT, XCD>), grid, dim3(kThreads), 0,
                      st, static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
-                     (uint32_t)groups, a.seg_len, a.coef);
+                     full_groups(a.n, a.seg_len, G), a.seg_len, a.coef);
+  const Tail t = tail_of(a.n, a.seg_len, G);
+  if (t.valid && (int)t.p != a.rank)
+    hipLaunchKernelGGL((k_quant_feedback_tail<BITS, IN_T, ST_T, G>), dim3(1),
+                       dim3(GroupMap<ST_T, G>::kLanes), 0, st, static_cast<const uint16_t*>(a.x),
+                       a.state, static_cast<uint8_t*>(a.segs.codes[t.p]), a.segs.params[t.p],
+                       (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
 }
 
 template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool XCD>
@@ -499,8 +682,14 @@ void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock, grid_x));
   hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NT, NTP, XCD>), grid,
                      dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, a.segs,
-                     a.P, a.rank, (uint32_t)groups, a.seg_len,
+                     a.P, a.rank, full_groups(a.n, a.seg_len, G), a.seg_len,
                      static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
+  const Tail t = tail_of(a.n, a.seg_len, G);
+  if (t.valid && (int)t.p == a.rank)
+    hipLaunchKernelGGL((k_owner_reduce_requant_tail<BITS, IN_T, ST_T, OUT_T, G>), dim3(1),
+                       dim3(GroupMap<ST_T, G>::kLanes), 0, st, static_cast<const uint16_t*>(a.x),
+                       a.state, a.segs, a.P, a.rank, static_cast<uint8_t*>(a.out_codes),
+                       a.out_params, (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
 }
 
 template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
@@ -509,7 +698,7 @@ void launch_k3(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   constexpr int gpb = (kThreads / 64) * GatherMap<OUT_T, G>::kGroupsPerWave * CH;
   dim3 grid(blocks_for(groups, gpb, grid_x), (unsigned)a.P);
   hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>), grid, dim3(kThreads), 0, st,
-                     a.segs, (uint32_t)groups, a.seg_len, a.out);
+                     a.segs, a.n, a.seg_len, a.out);
 }
 
 // Nontemporal loads and stores for every streamed array, except the owner

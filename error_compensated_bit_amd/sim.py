@@ -33,23 +33,21 @@ class Ranks:
     owned: list     # owned[o]: owner o's requantized payload
     out: torch.Tensor
 
-    @property
-    def seg_len(self) -> int:
-        return self.n // self.P
+    seg_len: int = 0
 
 
 def alloc_ranks(cfg: B.echo_config, P: int, n: int, device, bits_max: int | None = None) -> Ranks:
     """Buffers for P ranks; payloads are sized for `bits_max` (default cfg.bits)
     so one set of buffers serves calls of different widths."""
     bits = bits_max or cfg.bits
-    seg = n // P
+    seg = B.echo_segment_len(n, P, cfg.group)
     sdt = state_torch_dtype(cfg)
     state = [torch.empty(2 * n, dtype=sdt, device=device) for _ in range(P)]
     sent = [[None if o == p else B.alloc_payload(seg, bits, device, group=cfg.group)
              for o in range(P)] for p in range(P)]
     owned = [B.alloc_payload(seg, bits, device, group=cfg.group) for _ in range(P)]
     out = torch.empty(n, dtype=out_torch_dtype(cfg), device=device)
-    r = Ranks(P, n, state, sent, owned, out)
+    r = Ranks(P, n, state, sent, owned, out, seg)
     for p in range(P):
         B.echo_state_reset(cfg, state[p], n)
     return r

@@ -22,14 +22,21 @@
  *          parameters).
  *
  * Layout (every call):
- *   - A message of n elements per rank is split into P equal contiguous
- *     segments; rank p owns segment p = [p*n/P, (p+1)*n/P).
+ *   - A message of n >= 1 elements per rank is split into P contiguous
+ *     segments of whole groups: seg_len = echo_segment_len(n, P, group) =
+ *     ceil(ceil(n/P) / group) * group, and rank p owns segment p =
+ *     [p*seg_len, min((p+1)*seg_len, n)).  When n is a multiple of P*group
+ *     every segment holds n/P elements; otherwise the last non-empty segment
+ *     ends in a partial group (quantized over its valid elements) and the
+ *     segments after it are empty.
  *   - Groups of `group` consecutive elements of a segment (128 by default;
  *     32 and 64 are also accepted) share one scale and one zero point, both
  *     IEEE binary16; params[g] = scale | zero << 16.
- *   - Codes: bits = 4 -> two per byte, the even element in the low nibble;
- *     bits = 8 -> one per byte.  Codes and params of a segment are two
- *     separate arrays ("payload", echo_seg).
+ *   - Codes: bits = 4 -> two per byte, the even element in the low nibble
+ *     (an odd-length segment leaves its last high nibble 0); bits = 8 -> one
+ *     per byte.  Codes and params of a segment are two separate arrays
+ *     ("payload", echo_seg), always sized for seg_len elements:
+ *     echo_codes_bytes(seg_len, bits) and echo_params_bytes(seg_len, group).
  *   - Dequantized value = fma(code, scale, zero) in fp32.
  *   - Error state: one array per rank of 2n elements of the config's
  *     state type (fp32 or bf16) holding the short memory S and the long
@@ -63,7 +70,7 @@ extern "C" {
 /* return codes */
 #define ECHO_OK          0
 #define ECHO_ERR_ARG    -1   /* null pointer, unsupported or out-of-range parameter */
-#define ECHO_ERR_SHAPE  -2   /* n not a positive multiple of P * group, or n/P > 2^31 groups */
+#define ECHO_ERR_SHAPE  -2   /* n <= 0, or a segment of more than 2^31 groups */
 #define ECHO_ERR_ALIGN  -3   /* a buffer pointer is not 16-byte aligned */
 #define ECHO_ERR_HIP    -4   /* the HIP runtime reported an error at launch */
 
@@ -90,7 +97,7 @@ typedef struct echo_config {
     float   mix_long;    /* share of each residual given to the long memory, in [0, 1] */
 } echo_config;
 
-/* One segment's payload: codes (n/P * bits/8 bytes) and params (n/P/group words). */
+/* One segment's payload: codes (seg_len * bits/8 bytes) and params (seg_len/group words). */
 typedef struct echo_seg {
     void*     codes;
     uint32_t* params;
@@ -122,7 +129,8 @@ int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* strea
  *   echo_owner_reduce_requant); P = 1 launches nothing.
  *   x: device, n 16-bit elements (in_dtype).  state: device, n (S, L) pairs.
  *   out: host array of P echo_seg; out[rank] is ignored, every other entry
- *   must point at a payload sized for n/P elements.
+ *   must point at a payload sized for seg_len elements (nothing is written
+ *   for an empty segment).
  *   Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_ALIGN, ECHO_ERR_HIP.
  */
 int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n,
@@ -160,8 +168,10 @@ int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n
 int echo_dequant_gather(const echo_config* cfg, int P, int64_t n,
                         const echo_seg* in, void* out, void* stream);
 
-/* Buffer sizes (0 for invalid input): payload of a segment of seg_len
- * elements, and the error state of an n-element message. */
+/* Sizes (0 for invalid input): the segment length of an n-element message
+ * over P ranks, the payload of a segment of seg_len elements, and the error
+ * state of an n-element message. */
+int64_t echo_segment_len(int64_t n, int P, int group);
 size_t echo_codes_bytes(int64_t seg_len, int bits);
 size_t echo_params_bytes(int64_t seg_len, int group);
 size_t echo_state_bytes(int64_t n, int state_dtype);

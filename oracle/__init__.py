@@ -95,6 +95,20 @@ def codes_bytes(seg_len: int, bits: int) -> int:
     return seg_len * bits // 8
 
 
+def segment_len(n: int, P: int, group: int) -> int:
+    """Elements per segment: ceil(n/P) rounded up to whole groups; segment p is
+    [p*seg_len, min((p+1)*seg_len, n)), so only the last non-empty segment can
+    end in a partial group and trailing segments may be empty."""
+    per = -(-n // P)
+    return -(-per // group) * group
+
+
+def segment_range(n: int, P: int, group: int, p: int):
+    seg = segment_len(n, P, group)
+    lo = min(p * seg, n)
+    return lo, min(lo + seg, n) if p * seg < n else lo
+
+
 def state_np_dtype(cfg: Config):
     return np.float32 if cfg.state_dtype == STATE_F32 else np.uint16
 
@@ -179,8 +193,9 @@ def dequant_gather(cfg: Config, P: int, n: int, codes, params) -> np.ndarray:
 
 # ---------------------------------------------------------------- P simulated ranks
 def new_payload(cfg: Config, seg_len: int):
+    """Payload buffers for a segment of seg_len elements (whole groups)."""
     return (np.zeros(codes_bytes(seg_len, cfg.bits), np.uint8),
-            np.zeros(seg_len // cfg.group, np.uint32))
+            np.zeros(-(-seg_len // cfg.group), np.uint32))
 
 
 def allreduce(cfg: Config, xs, Ss, Ls, qpass=None):
@@ -195,7 +210,7 @@ def allreduce(cfg: Config, xs, Ss, Ls, qpass=None):
     """
     P = len(xs)
     n = xs[0].size
-    seg = n // P
+    seg = segment_len(n, P, cfg.group)
     sent = [[None if o == p else new_payload(cfg, seg) for o in range(P)] for p in range(P)]
     k1_counts = [np.zeros(n, np.uint32) for _ in range(P)] if qpass is not None else None
     for p in range(P):
@@ -217,7 +232,8 @@ def allreduce(cfg: Config, xs, Ss, Ls, qpass=None):
         # contribution to the elements of its segment
         k2_all = np.zeros(n, np.uint32)
         for o in range(P):
-            k2_all[o * seg:(o + 1) * seg] = k2_counts[o][o * seg:(o + 1) * seg]
+            lo, hi = segment_range(n, P, cfg.group, o)
+            k2_all[lo:hi] = k2_counts[o][lo:hi]
         for p in range(P):
             qpass[p][:] = k1_counts[p] + k2_all
     return out, sent, owned

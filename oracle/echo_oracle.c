@@ -36,8 +36,13 @@
  *     0, qmax), dequant = fma(code, scale, zero); a scale that is not
  *     positive after rounding gives all codes 0 and dequant = zero;
  *     zero and scale are clamped to the finite fp16 range, -0 -> +0.
- *   - ownership: P equal contiguous segments, rank p owns segment p;
- *     groups are numbered within a segment in element order.
+ *   - ownership: P contiguous segments of seg_len = ceil(ceil(n/P)/G)*G
+ *     elements (whole groups), rank p owns segment p = [p*seg_len,
+ *     min((p+1)*seg_len, n)); only the last non-empty segment can end in a
+ *     partial group, and trailing segments may be empty.  Groups are
+ *     numbered within a segment in element order.  A partial group is
+ *     quantized over its valid elements; an INT4 segment of odd length
+ *     leaves the last byte's high nibble 0.
  *   - payload: INT4 codes two per byte, even element in the low nibble;
  *     INT8 one per byte; params[group] = scale_bits | zero_bits << 16.
  *   - owner sum: fp32, ranks in order 0..P-1, the owner's own term is its
@@ -269,15 +274,33 @@ static void eo_ema_update(void* S, void* L, int state_dtype, int64_t j, float r,
     eo_store_state(L, state_dtype, j, l_keep + l_new);
 }
 
+/* Segment length (whole groups) and the element count of segment p. */
+int64_t eo_segment_len(int64_t n, int P, int group)
+{
+    int64_t per = (n + P - 1) / P;
+    return (per + group - 1) / group * group;
+}
+
+static int64_t eo_segment_count(int64_t n, int64_t seg_len, int p)
+{
+    int64_t start = (int64_t)p * seg_len;
+    if (start >= n) return 0;
+    return (n - start) < seg_len ? (n - start) : seg_len;
+}
+
 static int eo_check_common(int bits, int group, int P, int64_t n)
 {
     if (bits != 4 && bits != 8) return EO_ERR_ARG;
-    if (group < 1 || P < 1 || P > 64 || n <= 0) return EO_ERR_ARG;
-    if (n % P != 0) return EO_ERR_SHAPE;
-    int64_t seg = n / P;
-    if (seg % group != 0) return EO_ERR_SHAPE;
-    if (bits == 4 && seg % 2 != 0) return EO_ERR_SHAPE;
+    if (group < 1 || group > 256 || P < 1 || P > 64 || n <= 0) return EO_ERR_ARG;
+    if (bits == 4 && group % 2 != 0) return EO_ERR_ARG;   /* groups start on byte boundaries */
     return EO_OK;
+}
+
+/* INT4: clear the code bytes of one group before its nibbles are written. */
+static void eo_clear_codes(uint8_t* codes, int bits, int64_t first, int glen)
+{
+    if (bits == 8) return;
+    for (int64_t b = first / 2; b < (first + glen + 1) / 2; ++b) codes[b] = 0;
 }
 
 /* ------------------------------------------------------------------ */
@@ -302,24 +325,26 @@ int eo_quantize_feedback(int bits, int group, int in_dtype, int state_dtype,
     if (rank < 0 || rank >= P) return EO_ERR_ARG;
     float aS, aL;
     eo_weights(bS, bL, lam, &aS, &aL);
-    const int64_t seg = n / P;
+    const int64_t seg = eo_segment_len(n, P, group);
     float v[256], deq[256];
     uint8_t q[256];
-    if (group > 256) return EO_ERR_ARG;
     for (int p = 0; p < P; ++p) {
         if (p == rank) continue;   /* the owned segment is never quantized here */
-        for (int64_t gi = 0; gi < seg / group; ++gi) {
+        const int64_t len = eo_segment_count(n, seg, p);
+        for (int64_t gi = 0; gi * group < len; ++gi) {
             const int64_t base = (int64_t)p * seg + gi * group;
-            for (int i = 0; i < group; ++i) {
+            const int glen = (int)((len - gi * group) < group ? (len - gi * group) : group);
+            for (int i = 0; i < glen; ++i) {
                 int64_t j = base + i;
                 v[i] = eo_feedback_input(eo_load_in(x, in_dtype, j),
                                          eo_load_state(S, state_dtype, j),
                                          eo_load_state(L, state_dtype, j), eta);
             }
             uint16_t sh, zh;
-            eo_quantize_group(v, group, bits, q, &sh, &zh, deq);
+            eo_quantize_group(v, glen, bits, q, &sh, &zh, deq);
             params[p][gi] = (uint32_t)sh | ((uint32_t)zh << 16);
-            for (int i = 0; i < group; ++i) {
+            eo_clear_codes(codes[p], bits, gi * group, glen);
+            for (int i = 0; i < glen; ++i) {
                 int64_t j = base + i;
                 eo_put_code(codes[p], bits, gi * group + i, q[i]);
                 float r = v[i] - deq[i];
@@ -349,15 +374,16 @@ int eo_owner_reduce_requant(int bits, int group, int in_dtype, int state_dtype,
     int rc = eo_check_common(bits, group, P, n);
     if (rc) return rc;
     if (rank < 0 || rank >= P) return EO_ERR_ARG;
-    if (group > 256) return EO_ERR_ARG;
     float aS, aL;
     eo_weights(bS, bL, lam, &aS, &aL);
-    const int64_t seg = n / P;
+    const int64_t seg = eo_segment_len(n, P, group);
+    const int64_t len = eo_segment_count(n, seg, rank);
     float acc[256], deq[256];
     uint8_t q[256];
-    for (int64_t gi = 0; gi < seg / group; ++gi) {
+    for (int64_t gi = 0; gi * group < len; ++gi) {
         const int64_t base = (int64_t)rank * seg + gi * group;
-        for (int i = 0; i < group; ++i) {
+        const int glen = (int)((len - gi * group) < group ? (len - gi * group) : group);
+        for (int i = 0; i < glen; ++i) {
             const int64_t j = base + i;
             const int64_t k = gi * group + i;   /* index within the segment */
             float v_own = eo_feedback_input(eo_load_in(x, in_dtype, j),
@@ -373,9 +399,10 @@ int eo_owner_reduce_requant(int bits, int group, int in_dtype, int state_dtype,
             acc[i] = a;
         }
         uint16_t sh, zh;
-        eo_quantize_group(acc, group, bits, q, &sh, &zh, deq);
+        eo_quantize_group(acc, glen, bits, q, &sh, &zh, deq);
         out_params[gi] = (uint32_t)sh | ((uint32_t)zh << 16);
-        for (int i = 0; i < group; ++i) {
+        eo_clear_codes(out_codes, bits, gi * group, glen);
+        for (int i = 0; i < glen; ++i) {
             const int64_t j = base + i;
             eo_put_code(out_codes, bits, gi * group + i, q[i]);
             float o = (out_dtype == EO_OUT_BF16) ? eo_bf16_to_f32(eo_f32_to_bf16(deq[i]))
@@ -399,9 +426,10 @@ int eo_dequant_gather(int bits, int group, int out_dtype, int P, int64_t n,
 {
     int rc = eo_check_common(bits, group, P, n);
     if (rc) return rc;
-    const int64_t seg = n / P;
+    const int64_t seg = eo_segment_len(n, P, group);
     for (int p = 0; p < P; ++p) {
-        for (int64_t k = 0; k < seg; ++k) {
+        const int64_t len = eo_segment_count(n, seg, p);
+        for (int64_t k = 0; k < len; ++k) {
             float d = eo_dequant(eo_get_code(codes[p], bits, k), params[p][k / group]);
             int64_t j = (int64_t)p * seg + k;
             if (out_dtype == EO_OUT_BF16) ((uint16_t*)out)[j] = eo_f32_to_bf16(d);

@@ -260,7 +260,7 @@ def test_invalid_arguments_raise():
     state = torch.zeros(2048, device=DEV)
     out = [B.alloc_payload(512, 4, DEV) for _ in range(2)]
     with pytest.raises(B.EchoError) as e:
-        B.echo_quantize_feedback(cfg, 2, 0, 1000, x, state, out)
+        B.echo_quantize_feedback(cfg, 2, 0, 0, x, state, out)
     assert e.value.code == B.ECHO_ERR_SHAPE
     with pytest.raises(B.EchoError) as e:
         B.echo_quantize_feedback(cfg, 2, 0, 1024, x[1:], state, out)
@@ -269,3 +269,76 @@ def test_invalid_arguments_raise():
     with pytest.raises(B.EchoError) as e:
         B.echo_dequant_gather(bad, 2, 1024, out, x)
     assert e.value.code == B.ECHO_ERR_ARG
+
+
+# ------------------------------------------------------------------ ragged messages
+def valid_payload_bytes(n, P, group, bits, p):
+    """(code bytes, params) a segment holds: the rest of its buffer is never written."""
+    lo, hi = O.segment_range(n, P, group, p)
+    ln = hi - lo
+    return -(-ln * bits // 8), -(-ln // group)
+
+
+@pytest.mark.parametrize("P,group,n,bits,state_dtype,out_dtype", [
+    (4, 128, 1000, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
+    (3, 32, 1001, 4, B.ECHO_STATE_BF16, B.ECHO_OUT_BF16),
+    (8, 128, 300, 8, B.ECHO_STATE_F32, B.ECHO_OUT_F32),
+    (2, 64, 7, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
+    (5, 32, 129, 8, B.ECHO_STATE_BF16, B.ECHO_OUT_F32),
+    (16, 128, 2049, 4, B.ECHO_STATE_BF16, B.ECHO_OUT_BF16),
+    (1, 64, 1111, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
+    (8, 128, 8 * 128 * 37 + 5, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
+])
+def test_ragged_allreduce_two_calls(P, group, n, bits, state_dtype, out_dtype):
+    """n not a multiple of P*group: the last non-empty segment ends in a
+    partial group and later segments are empty.  Every payload byte a
+    segment holds, the output and every state match the oracle; payload
+    bytes past a segment's end keep their sentinel."""
+    banner(f"ragged P={P} group={group} n={n} bits={bits}")
+    rng = np.random.default_rng(n + P + group)
+    cfg = B.make_config(bits=bits, group=group, state_dtype=state_dtype, out_dtype=out_dtype)
+    ocfg = oracle_config(cfg)
+    seg = B.echo_segment_len(n, P, group)
+    assert seg == O.segment_len(n, P, group)
+    r = sim.alloc_ranks(cfg, P, n, DEV)
+    for p in range(P):
+        for pay in [r.owned[p]] + [r.sent[p][o] for o in range(P) if o != p]:
+            pay.codes.fill_(0xA5)
+            pay.params.view(torch.uint8).fill_(0xA5)
+    oS = [np.zeros(n, O.state_np_dtype(ocfg)) for _ in range(P)]
+    oL = [np.zeros(n, O.state_np_dtype(ocfg)) for _ in range(P)]
+    for site in range(2):
+        xb = [rand_input(rng, n, B.ECHO_IN_BF16, scale=1.0 + site)[0] for _ in range(P)]
+        sim.allreduce(cfg, r, [device_bits16(a, torch.bfloat16, DEV) for a in xb])
+        torch.cuda.synchronize()
+        out, sent, owned = O.allreduce(ocfg, xb, oS, oL)
+        for o in range(P):
+            cb, pb = valid_payload_bytes(n, P, group, bits, o)
+            pays = [(r.owned[o], owned[o], "owned")] + [(r.sent[p][o], sent[p][o], f"sent {p}")
+                                                        for p in range(P) if p != o]
+            for gpu_pay, ora_pay, tag in pays:
+                c, q = host(gpu_pay.codes), host(gpu_pay.params)
+                assert_bits_equal(c[:cb], ora_pay[0][:cb], f"{tag}->{o} codes")
+                assert_bits_equal(q[:pb], ora_pay[1][:pb], f"{tag}->{o} params")
+                assert np.all(c[cb:] == 0xA5), f"{tag}->{o}: codes written past the segment"
+                assert np.all(q[pb:].view(np.uint8) == 0xA5), f"{tag}->{o}: params written past the segment"
+        for p in range(P):
+            cmp_state(r.state[p], oS[p], oL[p], f"rank {p} site {site}")
+        assert_bits_equal(host(r.out), out, "output")
+
+
+@pytest.mark.parametrize("group,n,P", [(128, 1000, 4), (32, 77, 2), (64, 65, 1)])
+def test_ragged_gather_does_not_write_past_n(group, n, P):
+    rng = np.random.default_rng(n)
+    cfg = B.make_config(group=group)
+    seg = B.echo_segment_len(n, P, group)
+    pls = [random_payload_host(rng, seg, 4, group) for _ in range(P)]
+    inp = [to_device_payload(c, q, DEV) for c, q in pls]
+    out = torch.empty(n + 40, dtype=torch.bfloat16, device=DEV)
+    out.view(torch.uint8).fill_(0x77)
+    B.echo_dequant_gather(cfg, P, n, inp, out[:n])
+    torch.cuda.synchronize()
+    ref = O.dequant_gather(oracle_config(cfg), P, n, [c for c, _ in pls], [q for _, q in pls])
+    got = host(out)
+    assert_bits_equal(got[:n], ref, "output")
+    assert np.all(got[n:].view(np.uint8) == 0x77)

@@ -282,3 +282,92 @@ def test_payload_ratio_matches_the_stated_ceiling():
     seg = G * 16
     codes, params = O.new_payload(O.Config(), seg)
     assert (codes.nbytes + params.nbytes) * 8 / seg == payload_bits
+
+
+# --------------------------------------------------------------- ragged messages
+# n not a multiple of P * group: segments of whole groups, the last non-empty
+# one ends in a partial group, trailing ones may be empty (a reading of the
+# pages, which fix no layout).
+RAGGED = [(4, 128, 1000), (3, 32, 1000), (8, 128, 300), (2, 64, 7), (5, 32, 129), (16, 128, 2049)]
+
+
+@pytest.mark.parametrize("P,group,n", RAGGED)
+def test_ragged_at_most_two_quantizations(P, group, n):
+    rng = np.random.default_rng(n + P)
+    xs = [rand_bf16(rng, n) for _ in range(P)]
+    Ss, Ls = fresh_state(P, n)
+    qpass = [np.zeros(n, np.uint32) for _ in range(P)]
+    O.allreduce(O.Config(group=group), xs, Ss, Ls, qpass=qpass)
+    for p in range(P):
+        lo, hi = O.segment_range(n, P, group, p)
+        assert np.all(qpass[p][lo:hi] == 1)
+        other = np.ones(n, bool)
+        other[lo:hi] = False
+        assert np.all(qpass[p][other] == 2)
+
+
+@pytest.mark.parametrize("P,group,n", RAGGED)
+def test_ragged_residuals_sum_to_negated_injected_error(P, group, n):
+    cfg = O.Config(group=group, beta_short=0.0, mix_long=0.0)
+    rng = np.random.default_rng(7 * n + P)
+    xs = [rand_bf16(rng, n, t=4) for _ in range(P)]
+    Ss, Ls = fresh_state(P, n)
+    out, _, _ = O.allreduce(cfg, xs, Ss, Ls)
+    xsum = sum(bf16_to_f64(x) for x in xs)
+    e = out_to_f64(out, cfg) - xsum
+    rsum = sum(S.astype(np.float64) for S in Ss)
+    abs_terms = sum(np.abs(bf16_to_f64(x)) for x in xs) + np.abs(xsum) + np.abs(e)
+    assert np.all(np.abs(rsum + e) <= (2 * P + 2) * 2.0 ** -24 * abs_terms)
+
+
+@pytest.mark.parametrize("P,group,n", RAGGED)
+def test_ragged_identical_integer_inputs_sum_exactly(P, group, n):
+    rng = np.random.default_rng(3 * n)
+    k = rng.integers(0, 16, size=n)
+    seg = O.segment_len(n, P, group)
+    for p in range(P):                      # every group, partial ones too, spans 0..15
+        lo, hi = O.segment_range(n, P, group, p)
+        for g0 in range(lo, hi, group):
+            k[g0] = 0
+            if g0 + 1 < hi:
+                k[g0 + 1] = 15
+    x = O.f32_to_bf16_bits(k.astype(np.float32))
+    Ss, Ls = fresh_state(P, n)
+    out, _, owned = O.allreduce(O.Config(group=group), [x.copy() for _ in range(P)], Ss, Ls)
+    # (a one-element last group is a constant group: exact too, zero = the value)
+    assert np.array_equal(out_to_f64(out, O.Config()), P * k.astype(np.float64))
+    assert seg % group == 0
+
+
+@pytest.mark.parametrize("group,n", [(128, 300), (32, 77), (64, 65)])
+def test_ragged_single_rank_round_trip_per_group(group, n):
+    cfg = O.Config(group=group, out_dtype=O.OUT_F32)
+    rng = np.random.default_rng(n)
+    x = rand_bf16(rng, n, t=4)
+    Ss, Ls = fresh_state(1, n)
+    out, _, owned = O.allreduce(cfg, [x], Ss, Ls)
+    xf = bf16_to_f64(x).astype(np.float32)
+    for gi, g0 in enumerate(range(0, n, group)):
+        sl = slice(g0, min(g0 + group, n))
+        q, sb, zb, deq = O.quantize_group(xf[sl], 4)
+        assert np.array_equal(out[sl], deq)
+        assert owned[0][1][gi] == (sb | (zb << 16))
+        unpacked = np.stack([owned[0][0] & 0x0F, owned[0][0] >> 4], axis=1).reshape(-1)
+        assert np.array_equal(unpacked[sl], q)
+    # the unused high nibble of an odd-length INT4 segment is 0
+    if n % 2:
+        assert owned[0][0][n // 2] >> 4 == 0
+
+
+def test_ragged_empty_segments():
+    """n = 100 over P = 4 with groups of 128: only rank 0 owns elements."""
+    P, group, n = 4, 128, 100
+    assert [O.segment_range(n, P, group, p) for p in range(P)] == [(0, 100)] + [(100, 100)] * 3
+    rng = np.random.default_rng(5)
+    xs = [rand_bf16(rng, n) for _ in range(P)]
+    Ss, Ls = fresh_state(P, n)
+    out, sent, owned = O.allreduce(O.Config(group=group), xs, Ss, Ls)
+    for o in range(1, P):
+        assert not owned[o][0].any() and not owned[o][1].any()
+    xsum = sum(bf16_to_f64(x) for x in xs)
+    assert np.abs(out_to_f64(out, O.Config()) - xsum).max() < 0.5 * np.abs(xsum).max()
