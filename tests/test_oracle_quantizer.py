@@ -235,3 +235,27 @@ def test_packed_payload_layout(bits):
     assert np.array_equal(unpacked, k.astype(np.uint8))
     assert np.all(params[0] == 0x3C00)   # scale 1.0 (0x3C00), zero 0.0
     assert not S.any() and not L.any()   # lossless: zero residual
+
+
+def test_payload_bytes_do_not_depend_on_prior_buffer_contents():
+    """The codes of a segment are fully written from scratch (INT4 bytes
+    are rebuilt, not merged into old contents); an odd-length segment's last
+    high nibble is 0."""
+    P, rank, group, n = 2, 0, 32, 159       # segment 1 (rank 0 quantizes it) holds 63 elements
+    rng = np.random.default_rng(8)
+    x = O.f32_to_bf16_bits(rng.normal(size=n).astype(np.float32))
+    seg = O.segment_len(n, P, group)
+    assert seg == 96 and O.segment_range(n, P, group, 1) == (96, 159)
+    outs = []
+    for fill in (0x00, 0xFF, 0x5A):
+        S = np.zeros(n, np.float32)
+        L = np.zeros(n, np.float32)
+        codes = [None, np.full(seg // 2, fill, np.uint8)]
+        params = [None, np.full(seg // group, 0xFFFFFFFF, np.uint32)]
+        O.quantize_feedback(O.Config(group=group), P, rank, x, S, L, codes, params)
+        written = -(-63 // 2)                                  # bytes of 63 codes
+        assert np.all(codes[1][written:] == fill)              # nothing past the segment
+        outs.append((codes[1][:written].copy(), params[1][:2].copy()))
+    for c, q in outs[1:]:
+        assert np.array_equal(c, outs[0][0]) and np.array_equal(q, outs[0][1])
+    assert outs[0][0][-1] >> 4 == 0                            # 63rd code: high nibble 0
