@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -66,6 +67,20 @@ def kernel_source_digest() -> str:
         h.update(open(f, "rb").read())
     h.update(" ".join(eb.hipcc_flags()).encode())
     return h.hexdigest()[:16]
+
+
+def input_digests(xs):
+    """SHA-256 (first 16 hex digits) of every rank's input bytes: the bytes,
+    not the seeds, define a run's input."""
+    import torch
+    out = []
+    for x in xs:
+        h = hashlib.sha256()
+        flat = x.reshape(-1)
+        for i in range(0, flat.numel(), 1 << 27):
+            h.update(flat[i:i + (1 << 27)].view(torch.int16).cpu().numpy().tobytes())
+        out.append(h.hexdigest()[:16])
+    return out
 
 
 def traffic_from_profile(workload: str, kernel: str):
@@ -316,6 +331,7 @@ def main():
     wall = time.perf_counter() - t0
     k_ms = {k: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / args.steps
             for j, k in enumerate(KERNELS)}
+    ev_steps = sorted(ev[0].elapsed_time(ev[3]) for ev in events)
     ms_per_step = wall * 1e3 / args.steps
     ms_eager = ms_per_step
     ms_graph = None
@@ -367,9 +383,12 @@ def main():
                    "group": args.group, "state": args.state, "input": "bf16", "output": "bf16",
                    "eta": cfg.eta, "beta_short": cfg.beta_short, "beta_long": cfg.beta_long,
                    "mix_long": round(cfg.mix_long, 6),
-                   "algorithmic_bytes_per_step": int(alg_total)},
+                   "algorithmic_bytes_per_step": int(alg_total),
+                   "input_sha256": input_digests(xs)},
         "kernel_ms": {k: round(v, 5) for k, v in k_ms.items()},
         "ms_per_step_eager": round(ms_eager, 5),
+        "ms_step_events": {"median": round(statistics.median(ev_steps), 5),
+                           "min": round(ev_steps[0], 5)},
         "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -19,13 +19,24 @@
 // gfx950 this streams markedly faster than two separate S and L arrays.
 //
 // Thread mapping of the entry and owner passes: EPL consecutive elements per
-// lane (2 for fp32 state, 4 for bf16 state), so a group of 128 elements is
-// one wave (fp32) or one half-wave (bf16), and every wave-wide load or store
-// of the state is 1 KiB contiguous.  The group min/max is a butterfly of DPP
-// moves and a ds_swizzle inside each 32-lane half, plus, for a whole-wave
-// group, a readlane of lanes 0 and 32.  Streamed arrays use nontemporal
-// loads and stores.  One group per wave (or half-wave) per launch slot, with
-// enough blocks to cover the segment: short-lived waves stream best here.
+// lane (2 for fp32 state, 4 for bf16 state), so a group of G elements (32,
+// 64 or 128) is an aligned run of G/EPL lanes -- one whole wave for G = 128
+// with fp32 state -- and every wave-wide load or store of the state is 1 KiB
+// contiguous.  The group min/max is a butterfly of DPP moves and, for runs of
+// 32 or more lanes, a ds_swizzle; a whole-wave group then combines its two
+// halves with a readlane of lanes 0 and 32.  Streamed arrays use nontemporal
+// loads and stores.  Launches are one-shot, one group per lane run, with
+// enough blocks to cover a segment: short-lived waves stream best here.  The
+// owner pass numbers its blocks XCD-contiguously.
+//
+// A message whose length is not a multiple of P*G has one partial group (in
+// its last non-empty segment); the main entry and owner kernels handle whole
+// groups only and that group runs in a one-block tail kernel with element-wise
+// guarded accesses, so the streaming kernels carry no guarded path.  The
+// dequantize pass guards its last lane per element.
+//
+// Dequantize pass: 8 elements per lane for bf16 output, 4 for fp32 (one
+// 16-byte store either way), two chunks per lane one wave-width apart.
 //
 // Arithmetic is IEEE binary32 with no contraction (the library is built with
 // -ffp-contract=off); the only fused multiply-add is the dequantizer's

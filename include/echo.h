@@ -160,9 +160,12 @@ int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n
 /*
  * echo_dequant_gather -- turn the P owners' requantized payloads into the
  * all-reduce output ([JP-1]: the owner's requantized sum goes to every GPU).
- *   out[p*n/P + k] = dequant of in[p]'s code k, as out_dtype (bf16 round to
- *   nearest even, or fp32), for every p < P and k < n/P.
- *   in: host array of P echo_seg, all used.  out: device, n elements.
+ *   out[p*seg_len + k] = dequant of in[p]'s code k, as out_dtype (bf16
+ *   round to nearest even, or fp32), for every p < P and every k below the
+ *   element count of segment p (seg_len, fewer in the last non-empty
+ *   segment, none after it); nothing past out[n-1] is written.
+ *   in: host array of P echo_seg, every entry a valid payload (an empty
+ *   segment's payload is not read).  out: device, n elements.
  *   Errors: ECHO_ERR_ARG, ECHO_ERR_SHAPE, ECHO_ERR_ALIGN, ECHO_ERR_HIP.
  */
 int echo_dequant_gather(const echo_config* cfg, int P, int64_t n,

@@ -279,24 +279,29 @@ def valid_payload_bytes(n, P, group, bits, p):
     return -(-ln * bits // 8), -(-ln // group)
 
 
-@pytest.mark.parametrize("P,group,n,bits,state_dtype,out_dtype", [
-    (4, 128, 1000, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
-    (3, 32, 1001, 4, B.ECHO_STATE_BF16, B.ECHO_OUT_BF16),
-    (8, 128, 300, 8, B.ECHO_STATE_F32, B.ECHO_OUT_F32),
-    (2, 64, 7, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
-    (5, 32, 129, 8, B.ECHO_STATE_BF16, B.ECHO_OUT_F32),
-    (16, 128, 2049, 4, B.ECHO_STATE_BF16, B.ECHO_OUT_BF16),
-    (1, 64, 1111, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
-    (8, 128, 8 * 128 * 37 + 5, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16),
+F16, BF16 = B.ECHO_IN_F16, B.ECHO_IN_BF16
+
+
+@pytest.mark.parametrize("P,group,n,bits,state_dtype,out_dtype,in_dtype", [
+    (4, 128, 1000, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16, BF16),
+    (3, 32, 1001, 4, B.ECHO_STATE_BF16, B.ECHO_OUT_BF16, F16),
+    (8, 128, 300, 8, B.ECHO_STATE_F32, B.ECHO_OUT_F32, BF16),
+    (2, 64, 7, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16, BF16),
+    (5, 32, 129, 8, B.ECHO_STATE_BF16, B.ECHO_OUT_F32, F16),
+    (16, 128, 2049, 4, B.ECHO_STATE_BF16, B.ECHO_OUT_BF16, BF16),
+    (1, 64, 1111, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16, F16),
+    (8, 128, 8 * 128 * 37 + 5, 4, B.ECHO_STATE_F32, B.ECHO_OUT_BF16, BF16),
+    (6, 128, 6 * 128 * 11 + 6 * 128 - 1, 8, B.ECHO_STATE_F32, B.ECHO_OUT_BF16, F16),
 ])
-def test_ragged_allreduce_two_calls(P, group, n, bits, state_dtype, out_dtype):
+def test_ragged_allreduce_two_calls(P, group, n, bits, state_dtype, out_dtype, in_dtype):
     """n not a multiple of P*group: the last non-empty segment ends in a
     partial group and later segments are empty.  Every payload byte a
     segment holds, the output and every state match the oracle; payload
     bytes past a segment's end keep their sentinel."""
     banner(f"ragged P={P} group={group} n={n} bits={bits}")
     rng = np.random.default_rng(n + P + group)
-    cfg = B.make_config(bits=bits, group=group, state_dtype=state_dtype, out_dtype=out_dtype)
+    cfg = B.make_config(bits=bits, group=group, state_dtype=state_dtype, out_dtype=out_dtype,
+                        in_dtype=in_dtype)
     ocfg = oracle_config(cfg)
     seg = B.echo_segment_len(n, P, group)
     assert seg == O.segment_len(n, P, group)
@@ -308,8 +313,9 @@ def test_ragged_allreduce_two_calls(P, group, n, bits, state_dtype, out_dtype):
     oS = [np.zeros(n, O.state_np_dtype(ocfg)) for _ in range(P)]
     oL = [np.zeros(n, O.state_np_dtype(ocfg)) for _ in range(P)]
     for site in range(2):
-        xb = [rand_input(rng, n, B.ECHO_IN_BF16, scale=1.0 + site)[0] for _ in range(P)]
-        sim.allreduce(cfg, r, [device_bits16(a, torch.bfloat16, DEV) for a in xb])
+        xb = [rand_input(rng, n, in_dtype, scale=1.0 + site)[0] for _ in range(P)]
+        tdt = torch.float16 if in_dtype == F16 else torch.bfloat16
+        sim.allreduce(cfg, r, [device_bits16(a, tdt, DEV) for a in xb])
         torch.cuda.synchronize()
         out, sent, owned = O.allreduce(ocfg, xb, oS, oL)
         for o in range(P):
