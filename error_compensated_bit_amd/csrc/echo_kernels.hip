@@ -447,7 +447,7 @@ __global__ void k_quant_feedback_tail(const uint16_t* __restrict__ x, void* __re
 // Owner pass over segment `rank` ([JP-1]: sum in fp32 in rank order with the
 // owner's own unquantized term, requantize; [JP-W] the round trip; [JP-2]
 // the owner's residual against the output value, state update fused).
-template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool FULL>
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G, int NP, bool NT, bool NTP, bool FULL>
 __device__ __forceinline__ void owner_group(const uint16_t* __restrict__ x, void* __restrict__ state,
                                             const SegTable& in, int P, int rank,
                                             uint8_t* __restrict__ out_codes,
@@ -457,16 +457,18 @@ __device__ __forceinline__ void owner_group(const uint16_t* __restrict__ x, void
   constexpr int E = M::kEPL;
   const uint64_t k = (uint64_t)g * G + lane * E;
   const uint64_t e = base + k;
-  // incoming payload words first, so that all loads are in flight together
-  // (a payload is sized for a full segment: the word of a partial group
-  // exists, its bytes past the group's end are ignored)
-  uint32_t cw[kMaxRanks], pw[kMaxRanks];
+  // Incoming payload words first, so that all loads are in flight together.
+  // NP >= P slots are loaded without a branch: the launcher points the
+  // owner's own slot and the slots from P on at another rank's payload, and
+  // those words are ignored.  (Loads under a per-slot branch made the
+  // compiler wait for the first one before issuing the rest.)  A payload is
+  // sized for a full segment: the word of a partial group exists, its bytes
+  // past the group's end are ignored.
+  uint32_t cw[NP], pw[NP];
 #pragma unroll
-  for (int p = 0; p < kMaxRanks; ++p) {
-    if (p < P && p != rank) {
-      cw[p] = CodeIO<BITS, E>::template load<NTP>(static_cast<const uint8_t*>(in.codes[p]), k);
-      pw[p] = in.params[p][g];
-    }
+  for (int p = 0; p < NP; ++p) {
+    cw[p] = CodeIO<BITS, E>::template load<NTP>(static_cast<const uint8_t*>(in.codes[p]), k);
+    pw[p] = in.params[p][g];
   }
   float xv[E], s[E], l[E], acc[E];
   if constexpr (FULL) {
@@ -476,8 +478,13 @@ __device__ __forceinline__ void owner_group(const uint16_t* __restrict__ x, void
     load_in_part<IN_T, E>(x + e, xv, nv);
     load_state_part<ST_T>(state, e, s, l, nv);
   }
+  // Keep every payload load here, ahead of the per-slot branches below:
+  // without this use the compiler sinks a slot's load into its branch, and
+  // the wave then waits for it before issuing the next.
 #pragma unroll
-  for (int p = 0; p < kMaxRanks; ++p) {
+  for (int p = 0; p < NP; ++p) asm volatile("" ::"v"(cw[p]), "v"(pw[p]));
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
     if (p < P) {
       if (p == rank) {
 #pragma unroll
@@ -525,7 +532,7 @@ __device__ __forceinline__ void owner_group(const uint16_t* __restrict__ x, void
 
 // Full groups only (see k_quant_feedback); the partial group goes to
 // k_owner_reduce_requant_tail.
-template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool XCD>
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G, int NP, bool NT, bool NTP, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable in, int P, int rank,
     FullGroups fg, uint64_t seg_len, uint8_t* __restrict__ out_codes,
@@ -535,9 +542,9 @@ __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
   const uint32_t bx = XCD ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
   const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
   if (g >= fg.of((uint32_t)rank)) return;
-  owner_group<BITS, IN_T, ST_T, OUT_T, G, NT, NTP, true>(x, state, in, P, rank, out_codes,
-                                                         out_params, g, lane,
-                                                         (uint64_t)rank * seg_len, M::kEPL, c);
+  owner_group<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, true>(x, state, in, P, rank, out_codes,
+                                                             out_params, g, lane,
+                                                             (uint64_t)rank * seg_len, M::kEPL, c);
 }
 
 template <int BITS, int IN_T, int ST_T, int OUT_T, int G>
@@ -548,7 +555,7 @@ __global__ void k_owner_reduce_requant_tail(const uint16_t* __restrict__ x, void
                                             uint32_t g, uint32_t valid, Coef c) {
   using M = GroupMap<ST_T, G>;
   const int nv = (int)valid - (int)threadIdx.x * M::kEPL;
-  owner_group<BITS, IN_T, ST_T, OUT_T, G, false, false, false>(
+  owner_group<BITS, IN_T, ST_T, OUT_T, G, kMaxRanks, false, false, false>(
       x, state, in, P, rank, out_codes, out_params, g, threadIdx.x, base,
       nv < 0 ? 0 : nv > M::kEPL ? M::kEPL : nv, c);
 }
@@ -566,6 +573,18 @@ struct GatherMap {
   static constexpr int kGroupsPerWave = 64 / kLanes;
 };
 
+// The EPL codes of one lane and chunk: 4 bytes (INT4, bf16 out: 8 codes),
+// 2 bytes (INT4, fp32 out), 8 bytes (INT8, bf16 out) or 4 bytes (INT8, fp32).
+template <int BITS, int EPL, bool NT>
+__device__ __forceinline__ u32x2 gather_codes(const uint8_t* __restrict__ codes, uint64_t k) {
+  u32x2 w = {0u, 0u};
+  if constexpr (BITS == 4 && EPL == 8) w.x = ld<NT>(reinterpret_cast<const uint32_t*>(codes + k / 2));
+  else if constexpr (BITS == 4) w.x = ld<NT>(reinterpret_cast<const uint16_t*>(codes + k / 2));
+  else if constexpr (EPL == 8) w = ld<NT>(reinterpret_cast<const u32x2*>(codes + k));
+  else w.x = ld<NT>(reinterpret_cast<const uint32_t*>(codes + k));
+  return w;
+}
+
 template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
 __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint64_t n,
                                                              uint64_t seg_len, void* __restrict__ out) {
@@ -573,38 +592,37 @@ __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint64
   constexpr int EPL = M::kEPL;
   const int p = blockIdx.y;
   const uint64_t len = segment_count(n, seg_len, (uint32_t)p);
+  if (len == 0) return;   // an empty segment's payload is not read
   const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(in.codes[p]);
   const uint32_t* __restrict__ params = in.params[p];
   const uint64_t base = (uint64_t)p * seg_len;
+  const uint32_t last_g = (uint32_t)(seg_len / G) - 1;
   const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const uint32_t g0 = (blockIdx.x * (kThreads / 64) + wave) * M::kGroupsPerWave * CH;
+  const uint32_t in_group = (lane % M::kLanes) * EPL;
+  // Every chunk's loads go out before the first store, so a wave waits for
+  // memory once.  A chunk past the segment's end loads from a group index
+  // clamped into the payload (sized for seg_len elements) and stores nothing.
+  u32x2 cw[CH];
+  uint32_t pw[CH];
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) {
     const uint32_t g = g0 + ch * M::kGroupsPerWave + lane / M::kLanes;
-    const uint64_t k = (uint64_t)g * G + (lane % M::kLanes) * EPL;
+    const uint32_t gl = g < last_g ? g : last_g;
+    cw[ch] = gather_codes<BITS, EPL, NTP>(codes, (uint64_t)gl * G + in_group);
+    pw[ch] = params[gl];
+  }
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) {
+    const uint32_t g = g0 + ch * M::kGroupsPerWave + lane / M::kLanes;
+    const uint64_t k = (uint64_t)g * G + in_group;
     if (k >= len) break;   // lanes are independent here
-    const uint32_t pw = params[g];
-    const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
+    const float sf = f16_to_f32(pw[ch] & 0xffffu), zf = f16_to_f32(pw[ch] >> 16);
     float d[EPL];
-    if constexpr (BITS == 4 && EPL == 8) {
-      const uint32_t w = ld<NTP>(reinterpret_cast<const uint32_t*>(codes + k / 2));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) d[i] = decode((w >> (4 * i)) & 0xfu, sf, zf);
-    } else if constexpr (BITS == 4) {
-      const uint32_t w = ld<NTP>(reinterpret_cast<const uint16_t*>(codes + k / 2));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = decode((w >> (4 * i)) & 0xfu, sf, zf);
-    } else if constexpr (EPL == 8) {
-      const u32x2 w = ld<NTP>(reinterpret_cast<const u32x2*>(codes + k));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        d[i] = decode((w.x >> (8 * i)) & 0xffu, sf, zf);
-        d[4 + i] = decode((w.y >> (8 * i)) & 0xffu, sf, zf);
-      }
-    } else {
-      const uint32_t w = ld<NTP>(reinterpret_cast<const uint32_t*>(codes + k));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = decode((w >> (8 * i)) & 0xffu, sf, zf);
+    for (int i = 0; i < EPL; ++i) {
+      const uint32_t w = (BITS * i < 32) ? cw[ch].x : cw[ch].y;
+      d[i] = decode((w >> ((BITS * i) % 32)) & ((1u << BITS) - 1u), sf, zf);
     }
     if (k + EPL > len) {   // the last lane of a ragged message: element-wise stores
       const int nv = (int)(len - k);
@@ -687,19 +705,38 @@ void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
                        (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
 }
 
-template <int BITS, int IN_T, int ST_T, int OUT_T, int G, bool NT, bool NTP, bool XCD>
+// The incoming table as the owner pass reads it: the owner's own slot, which
+// the caller leaves unset, and every slot from P on point at another rank's
+// payload (the owner's outgoing one when P = 1), so that the kernel can load
+// a fixed number of slots without branches.
+SegTable owner_table(const LaunchArgs& a) {
+  SegTable t = a.segs;
+  const int other = (a.rank + 1) % a.P;
+  void* codes = a.P > 1 ? a.segs.codes[other] : a.out_codes;
+  uint32_t* params = a.P > 1 ? a.segs.params[other] : a.out_params;
+  for (int p = 0; p < kMaxRanks; ++p) {
+    if (p == a.rank || p >= a.P) {
+      t.codes[p] = codes;
+      t.params[p] = params;
+    }
+  }
+  return t;
+}
+
+template <int BITS, int IN_T, int ST_T, int OUT_T, int G, int NP, bool NT, bool NTP, bool XCD>
 void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
   const uint64_t groups = a.seg_len / G;
+  const SegTable in = owner_table(a);
   dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock, grid_x));
-  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NT, NTP, XCD>), grid,
-                     dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, a.segs,
+  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, XCD>), grid,
+                     dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, in,
                      a.P, a.rank, full_groups(a.n, a.seg_len, G), a.seg_len,
                      static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
   const Tail t = tail_of(a.n, a.seg_len, G);
   if (t.valid && (int)t.p == a.rank)
     hipLaunchKernelGGL((k_owner_reduce_requant_tail<BITS, IN_T, ST_T, OUT_T, G>), dim3(1),
                        dim3(GroupMap<ST_T, G>::kLanes), 0, st, static_cast<const uint16_t*>(a.x),
-                       a.state, a.segs, a.P, a.rank, static_cast<uint8_t*>(a.out_codes),
+                       a.state, in, a.P, a.rank, static_cast<uint8_t*>(a.out_codes),
                        a.out_params, (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
 }
 
@@ -742,6 +779,14 @@ template <typename F>
 void with_state(int v, F&& f) { if (v == kStateBF16) f(IC<kStateBF16>{}); else f(IC<kStateF32>{}); }
 template <typename F>
 void with_out(int v, F&& f) { if (v == kOutF32) f(IC<kOutF32>{}); else f(IC<kOutBF16>{}); }
+// Payload slots the owner pass loads: P rounded up to a power of two (>= 2).
+template <typename F>
+void with_slots(int P, F&& f) {
+  if (P <= 2) f(IC<2>{});
+  else if (P <= 4) f(IC<4>{});
+  else if (P <= 8) f(IC<8>{});
+  else f(IC<kMaxRanks>{});
+}
 
 void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
@@ -753,8 +798,9 @@ void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
 void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
     with_state(a.state_dtype, [&](auto S) { with_out(a.out_dtype, [&](auto O) {
-      launch_k2<B(), I(), S(), O(), G(), kNT, kNTOwnerPayload, kXcdOrderOwner>(a, 0, st);
-    }); }); }); }); });
+      with_slots(a.P, [&](auto NP) {
+        launch_k2<B(), I(), S(), O(), G(), NP(), kNT, kNTOwnerPayload, kXcdOrderOwner>(a, 0, st);
+      }); }); }); }); }); });
 }
 
 void run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
