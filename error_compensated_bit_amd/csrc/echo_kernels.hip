@@ -585,66 +585,110 @@ __device__ __forceinline__ u32x2 gather_codes(const uint8_t* __restrict__ codes,
   return w;
 }
 
+// Dequantize and store the EPL elements a lane holds for one chunk.
+template <int BITS, int OUT_T, int EPL, bool NT>
+__device__ __forceinline__ void gather_store(void* __restrict__ out, uint64_t e, u32x2 cw, uint32_t pw) {
+  const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
+  float d[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const uint32_t w = (BITS * i < 32) ? cw.x : cw.y;
+    d[i] = decode((w >> ((BITS * i) % 32)) & ((1u << BITS) - 1u), sf, zf);
+  }
+  if constexpr (OUT_T == kOutBF16) {
+    u32x4 o;
+    o.x = f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16);
+    o.y = f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16);
+    o.z = f32_to_bf16(d[4]) | (f32_to_bf16(d[5]) << 16);
+    o.w = f32_to_bf16(d[6]) | (f32_to_bf16(d[7]) << 16);
+    st<NT>(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + e), o);
+  } else {
+    f32x4 o = {d[0], d[1], d[2], d[3]};
+    st<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(out) + e), o);
+  }
+}
+
+template <int OUT_T, int G, int CH>
+constexpr uint32_t gather_groups_per_block() {
+  return (kThreads / 64) * GatherMap<OUT_T, G>::kGroupsPerWave * CH;
+}
+
+// Whole tiles of gather_groups_per_block() whole groups only: straight-line
+// code, every chunk's loads issued before the first store (a wave waits for
+// memory once).  The rest of each segment -- fewer than a tile of groups,
+// and the partial group of a ragged message -- goes to k_dequant_gather_tail.
 template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
-__global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, uint64_t n,
+__global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, FullGroups fg,
                                                              uint64_t seg_len, void* __restrict__ out) {
   using M = GatherMap<OUT_T, G>;
   constexpr int EPL = M::kEPL;
-  const int p = blockIdx.y;
-  const uint64_t len = segment_count(n, seg_len, (uint32_t)p);
-  if (len == 0) return;   // an empty segment's payload is not read
+  constexpr uint32_t kTile = gather_groups_per_block<OUT_T, G, CH>();
+  const uint32_t p = blockIdx.y;
+  if (blockIdx.x >= fg.of(p) / kTile) return;   // whole block
   const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(in.codes[p]);
   const uint32_t* __restrict__ params = in.params[p];
   const uint64_t base = (uint64_t)p * seg_len;
-  const uint32_t last_g = (uint32_t)(seg_len / G) - 1;
   const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const uint32_t g0 = (blockIdx.x * (kThreads / 64) + wave) * M::kGroupsPerWave * CH;
   const uint32_t in_group = (lane % M::kLanes) * EPL;
-  // Every chunk's loads go out before the first store, so a wave waits for
-  // memory once.  A chunk past the segment's end loads from a group index
-  // clamped into the payload (sized for seg_len elements) and stores nothing.
   u32x2 cw[CH];
   uint32_t pw[CH];
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) {
     const uint32_t g = g0 + ch * M::kGroupsPerWave + lane / M::kLanes;
-    const uint32_t gl = g < last_g ? g : last_g;
-    cw[ch] = gather_codes<BITS, EPL, NTP>(codes, (uint64_t)gl * G + in_group);
-    pw[ch] = params[gl];
+    cw[ch] = gather_codes<BITS, EPL, NTP>(codes, (uint64_t)g * G + in_group);
+    pw[ch] = params[g];
   }
 #pragma unroll
   for (int ch = 0; ch < CH; ++ch) {
     const uint32_t g = g0 + ch * M::kGroupsPerWave + lane / M::kLanes;
+    gather_store<BITS, OUT_T, EPL, NT>(out, base + (uint64_t)g * G + in_group, cw[ch], pw[ch]);
+  }
+}
+
+// One block per segment: the groups after its last whole tile, up to the
+// segment's end (the last non-empty segment may end in a partial group;
+// nothing past element n-1 is written).
+template <int BITS, int OUT_T, int G, int CH>
+__global__ __launch_bounds__(kThreads) void k_dequant_gather_tail(SegTable in, FullGroups fg,
+                                                                  uint64_t n, uint64_t seg_len,
+                                                                  void* __restrict__ out) {
+  using M = GatherMap<OUT_T, G>;
+  constexpr int EPL = M::kEPL;
+  constexpr uint32_t kTile = gather_groups_per_block<OUT_T, G, CH>();
+  const uint32_t p = blockIdx.y;
+  const uint64_t len = segment_count(n, seg_len, p);
+  if (len == 0) return;   // an empty segment's payload is not read
+  const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(in.codes[p]);
+  const uint32_t* __restrict__ params = in.params[p];
+  const uint64_t base = (uint64_t)p * seg_len;
+  const uint32_t first = fg.of(p) / kTile * kTile;
+  const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const uint32_t in_group = (lane % M::kLanes) * EPL;
+#pragma unroll
+  for (int ch = 0; ch < CH; ++ch) {
+    const uint32_t g = first + (wave * CH + ch) * M::kGroupsPerWave + lane / M::kLanes;
     const uint64_t k = (uint64_t)g * G + in_group;
     if (k >= len) break;   // lanes are independent here
-    const float sf = f16_to_f32(pw[ch] & 0xffffu), zf = f16_to_f32(pw[ch] >> 16);
-    float d[EPL];
+    const u32x2 cw = gather_codes<BITS, EPL, false>(codes, k);   // the payload holds seg_len codes
+    const uint32_t pw = params[g];
+    if (k + EPL <= len) {
+      gather_store<BITS, OUT_T, EPL, false>(out, base + k, cw, pw);
+      continue;
+    }
+    // the last lane of a ragged message: element-wise stores
+    const float sf = f16_to_f32(pw & 0xffffu), zf = f16_to_f32(pw >> 16);
+    const int nv = (int)(len - k);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
-      const uint32_t w = (BITS * i < 32) ? cw[ch].x : cw[ch].y;
-      d[i] = decode((w >> ((BITS * i) % 32)) & ((1u << BITS) - 1u), sf, zf);
-    }
-    if (k + EPL > len) {   // the last lane of a ragged message: element-wise stores
-      const int nv = (int)(len - k);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        if (i < nv) {
-          if constexpr (OUT_T == kOutBF16)
-            static_cast<uint16_t*>(out)[base + k + i] = (uint16_t)f32_to_bf16(d[i]);
-          else
-            static_cast<float*>(out)[base + k + i] = d[i];
-        }
+      if (i < nv) {
+        const uint32_t w = (BITS * i < 32) ? cw.x : cw.y;
+        const float d = decode((w >> ((BITS * i) % 32)) & ((1u << BITS) - 1u), sf, zf);
+        if constexpr (OUT_T == kOutBF16)
+          static_cast<uint16_t*>(out)[base + k + i] = (uint16_t)f32_to_bf16(d);
+        else
+          static_cast<float*>(out)[base + k + i] = d;
       }
-    } else if constexpr (OUT_T == kOutBF16) {
-      u32x4 o;
-      o.x = f32_to_bf16(d[0]) | (f32_to_bf16(d[1]) << 16);
-      o.y = f32_to_bf16(d[2]) | (f32_to_bf16(d[3]) << 16);
-      o.z = f32_to_bf16(d[4]) | (f32_to_bf16(d[5]) << 16);
-      o.w = f32_to_bf16(d[6]) | (f32_to_bf16(d[7]) << 16);
-      st<NT>(reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + base + k), o);
-    } else {
-      f32x4 o = {d[0], d[1], d[2], d[3]};
-      st<NT>(reinterpret_cast<f32x4*>(static_cast<float*>(out) + base + k), o);
     }
   }
 }
@@ -680,9 +724,8 @@ FullGroups full_groups(uint64_t n, uint64_t seg_len, int group) {
   return FullGroups{(uint32_t)(seg_len / group), t.p, t.g};
 }
 
-// Blocks along x: `grid_x` when given, else one launch slot per group.
-unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned grid_x) {
-  if (grid_x) return grid_x;
+// Blocks along x: enough for every group, one group per lane run.
+unsigned blocks_for(uint64_t groups, uint64_t groups_per_block) {
   const uint64_t b = (groups + groups_per_block - 1) / groups_per_block;
   return (unsigned)(b == 0 ? 1 : b);
 }
@@ -690,10 +733,10 @@ unsigned blocks_for(uint64_t groups, uint64_t groups_per_block, unsigned grid_x)
 }  // namespace
 
 template <int BITS, int IN_T, int ST_T, int G, bool NT, bool XCD>
-void launch_k1(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
+void launch_k1(const LaunchArgs& a, hipStream_t st) {
   const uint64_t groups = a.seg_len / G;
   const unsigned ny = (unsigned)(a.P - 1);
-  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock, grid_x), ny);
+  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock), ny);
   hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, G, NT, XCD>), grid, dim3(kThreads), 0,
                      st, static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
                      full_groups(a.n, a.seg_len, G), a.seg_len, a.coef);
@@ -724,10 +767,10 @@ SegTable owner_table(const LaunchArgs& a) {
 }
 
 template <int BITS, int IN_T, int ST_T, int OUT_T, int G, int NP, bool NT, bool NTP, bool XCD>
-void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
+void launch_k2(const LaunchArgs& a, hipStream_t st) {
   const uint64_t groups = a.seg_len / G;
   const SegTable in = owner_table(a);
-  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock, grid_x));
+  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock));
   hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, XCD>), grid,
                      dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, in,
                      a.P, a.rank, full_groups(a.n, a.seg_len, G), a.seg_len,
@@ -741,12 +784,16 @@ void launch_k2(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
 }
 
 template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
-void launch_k3(const LaunchArgs& a, unsigned grid_x, hipStream_t st) {
-  const uint64_t groups = a.seg_len / G;
-  constexpr int gpb = (kThreads / 64) * GatherMap<OUT_T, G>::kGroupsPerWave * CH;
-  dim3 grid(blocks_for(groups, gpb, grid_x), (unsigned)a.P);
-  hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>), grid, dim3(kThreads), 0, st,
-                     a.segs, a.n, a.seg_len, a.out);
+void launch_k3(const LaunchArgs& a, hipStream_t st) {
+  constexpr uint32_t tile = gather_groups_per_block<OUT_T, G, CH>();
+  const FullGroups fg = full_groups(a.n, a.seg_len, G);
+  const Tail t = tail_of(a.n, a.seg_len, G);
+  if (fg.all / tile > 0)
+    hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>), dim3(fg.all / tile, a.P),
+                       dim3(kThreads), 0, st, a.segs, fg, a.seg_len, a.out);
+  if (fg.all % tile || fg.in_last % tile || t.valid)
+    hipLaunchKernelGGL((k_dequant_gather_tail<BITS, OUT_T, G, CH>), dim3(1, a.P), dim3(kThreads), 0,
+                       st, a.segs, fg, a.n, a.seg_len, a.out);
 }
 
 // Nontemporal loads and stores for every streamed array, except the owner
@@ -791,7 +838,7 @@ void with_slots(int P, F&& f) {
 void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
     with_state(a.state_dtype, [&](auto S) {
-      launch_k1<B(), I(), S(), G(), kNT, kXcdOrderEntry>(a, 0, st);
+      launch_k1<B(), I(), S(), G(), kNT, kXcdOrderEntry>(a, st);
     }); }); }); });
 }
 
@@ -799,13 +846,13 @@ void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
     with_state(a.state_dtype, [&](auto S) { with_out(a.out_dtype, [&](auto O) {
       with_slots(a.P, [&](auto NP) {
-        launch_k2<B(), I(), S(), O(), G(), NP(), kNT, kNTOwnerPayload, kXcdOrderOwner>(a, 0, st);
+        launch_k2<B(), I(), S(), O(), G(), NP(), kNT, kNTOwnerPayload, kXcdOrderOwner>(a, st);
       }); }); }); }); }); });
 }
 
 void run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_out(a.out_dtype, [&](auto O) {
-    launch_k3<B(), O(), G(), kGatherChunks, kNT, kNT>(a, 0, st);
+    launch_k3<B(), O(), G(), kGatherChunks, kNT, kNT>(a, st);
   }); }); });
 }
 
