@@ -199,10 +199,28 @@ def copy_calibration(nbytes: int):
     log(f"copy calibration: {nbytes} bytes read and written per launch, 3 launches")
 
 
+def cpu_threads(P: int) -> int:
+    """Threads for the parallel oracle run: one per simulated rank, within the
+    cores this process may use (and at most 16, the host share of one GPU)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(P, avail, 16))
+
+
 def cpu_baseline(cfg, w, xs_dev, frac_den: int):
     """The CPU oracle on a bounded sample: the first 1/frac_den of every
     segment of every rank, one call from an empty state, all P ranks.
-    One rank's share = mean entry pass + mean owner pass + one gather."""
+
+    Timed twice on the same sample.  Single-threaded: one rank's share = mean
+    entry pass + mean owner pass + one gather.  Parallel: the P ranks' calls
+    are independent within each pass, so each pass runs them on a thread pool
+    (the oracle's C calls release the interpreter lock) and the host's
+    throughput is P shares of input over the wall time of the three passes.
+    `value` is the parallel figure, with `cores` threads."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle as O
     from error_compensated_bit_amd.inputs import bits16_numpy
@@ -216,35 +234,65 @@ def cpu_baseline(cfg, w, xs_dev, frac_den: int):
     ocfg = O.Config(bits=cfg.bits, group=cfg.group, eta=cfg.eta, beta_short=cfg.beta_short,
                     beta_long=cfg.beta_long, mix_long=cfg.mix_long, in_dtype=cfg.in_dtype,
                     out_dtype=cfg.out_dtype, state_dtype=cfg.state_dtype)
-    Ss = [np.zeros(ns, O.state_np_dtype(ocfg)) for _ in range(P)]
-    Ls = [np.zeros(ns, O.state_np_dtype(ocfg)) for _ in range(P)]
-    sent = [[None if o == p else O.new_payload(ocfg, sseg) for o in range(P)] for p in range(P)]
-    owned = [O.new_payload(ocfg, sseg) for _ in range(P)]
-    t_entry = t_owner = 0.0
-    for p in range(P):
-        t0 = time.perf_counter()
+
+    def fresh():
+        Ss = [np.zeros(ns, O.state_np_dtype(ocfg)) for _ in range(P)]
+        Ls = [np.zeros(ns, O.state_np_dtype(ocfg)) for _ in range(P)]
+        sent = [[None if o == p else O.new_payload(ocfg, sseg) for o in range(P)] for p in range(P)]
+        owned = [O.new_payload(ocfg, sseg) for _ in range(P)]
+        return Ss, Ls, sent, owned
+
+    def entry(p, Ss, Ls, sent):
         O.quantize_feedback(ocfg, P, p, xs[p], Ss[p], Ls[p],
                             [None if o == p else sent[p][o][0] for o in range(P)],
                             [None if o == p else sent[p][o][1] for o in range(P)])
-        t_entry += time.perf_counter() - t0
-    for o in range(P):
-        t0 = time.perf_counter()
+
+    def owner(o, Ss, Ls, sent, owned):
         O.owner_reduce_requant(ocfg, P, o, xs[o], Ss[o], Ls[o],
                                [None if p == o else sent[p][o][0] for p in range(P)],
                                [None if p == o else sent[p][o][1] for p in range(P)],
                                owned[o][0], owned[o][1])
+
+    def gather(owned):
+        return O.dequant_gather(ocfg, P, ns, [c for c, _ in owned], [q for _, q in owned])
+
+    # single-threaded
+    Ss, Ls, sent, owned = fresh()
+    t_entry = t_owner = 0.0
+    for p in range(P):
+        t0 = time.perf_counter()
+        entry(p, Ss, Ls, sent)
+        t_entry += time.perf_counter() - t0
+    for o in range(P):
+        t0 = time.perf_counter()
+        owner(o, Ss, Ls, sent, owned)
         t_owner += time.perf_counter() - t0
     t0 = time.perf_counter()
-    O.dequant_gather(ocfg, P, ns, [c for c, _ in owned], [q for _, q in owned])
+    out1 = gather(owned)
     t_gather = time.perf_counter() - t0
     t_share = t_entry / P + t_owner / P + t_gather
-    return {"value": round(2.0 * ns / t_share / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+    single = 2.0 * ns / t_share / 1e9
+
+    # parallel over ranks
+    T = cpu_threads(P)
+    Ss, Ls, sent, owned = fresh()
+    with ThreadPoolExecutor(max_workers=T) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(lambda p: entry(p, Ss, Ls, sent), range(P)))
+        list(pool.map(lambda o: owner(o, Ss, Ls, sent, owned), range(P)))
+        outs = list(pool.map(lambda p: gather(owned), range(P)))
+        t_par = time.perf_counter() - t0
+    if not all(np.array_equal(o, out1) for o in outs):
+        raise RuntimeError("parallel oracle run disagrees with the single-threaded one")
+    par = P * 2.0 * ns / t_par / 1e9
+    return {"value": round(par, 4), "unit": "GB/s", "cores": T, "kind": "oracle",
+            "single_core_value": round(single, 4),
             "sample": f"first {sseg} elements of every segment ({ns} of {n} elements per rank), "
-                      f"all {P} ranks, one call; share time {t_share:.2f} s "
-                      f"(entry {t_entry / P:.2f} + owner {t_owner / P:.2f} + gather {t_gather:.2f}); "
-                      f"single-threaded scalar C, total CPU time "
-                      f"{t_entry + t_owner + t_gather:.1f} s"}
+                      f"all {P} ranks, one call from an empty state. Parallel: the {P} ranks' "
+                      f"entry, owner and gather calls on {T} threads, {t_par:.2f} s wall for "
+                      f"{P} shares. Single-threaded: one share {t_share:.2f} s (entry "
+                      f"{t_entry / P:.2f} + owner {t_owner / P:.2f} + gather {t_gather:.2f}) "
+                      f"= {single:.4f} GB/s. Scalar C oracle."}
 
 
 def main():
