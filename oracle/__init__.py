@@ -52,7 +52,7 @@ def lib() -> ctypes.CDLL:
         L.eo_quantize_feedback.argtypes = [i32, i32, i32, i32, f32, f32, f32, f32,
                                            i32, i32, i64, P, P, P, P, P, P]
         L.eo_owner_reduce_requant.argtypes = [i32, i32, i32, i32, i32, f32, f32, f32, f32,
-                                              i32, i32, i64, P, P, P, P, P, P, P, P]
+                                              i32, i32, i64, P, P, P, P, P, P, P, P, P]
         L.eo_dequant_gather.argtypes = [i32, i32, i32, i32, i64, P, P, P]
         L.eo_state_reset.argtypes = [P, P, i32, i64]
         for name in ("eo_quantize_feedback", "eo_owner_reduce_requant",
@@ -171,15 +171,20 @@ def quantize_feedback(cfg: Config, P: int, rank: int, x: np.ndarray, S: np.ndarr
 
 def owner_reduce_requant(cfg: Config, P: int, rank: int, x: np.ndarray, S: np.ndarray,
                          L: np.ndarray, in_codes, in_params, out_codes: np.ndarray,
-                         out_params: np.ndarray, qpass: np.ndarray | None = None):
-    """Owner pass of `rank` over its segment: fills out_codes/out_params; updates S, L."""
+                         out_params: np.ndarray, qpass: np.ndarray | None = None,
+                         acc: np.ndarray | None = None):
+    """Owner pass of `rank` over its segment: fills out_codes/out_params; updates S, L.
+    acc (optional, float32, one per element of the segment) receives the fp32
+    sum before requantization."""
     n = x.size
+    if acc is not None:
+        assert acc.dtype == np.float32 and acc.size >= segment_len(n, P, cfg.group)
     rc = lib().eo_owner_reduce_requant(cfg.bits, cfg.group, cfg.in_dtype, cfg.state_dtype,
                                        cfg.out_dtype, cfg.eta, cfg.beta_short,
                                        cfg.beta_long, cfg.mix_long, P, rank, n,
                                        _ptr(x), _ptr(S), _ptr(L), _ptr_array(in_codes),
                                        _ptr_array(in_params), _ptr(out_codes),
-                                       _ptr(out_params), _ptr(qpass))
+                                       _ptr(out_params), _ptr(qpass), _ptr(acc))
     _check(rc, "owner_reduce_requant")
 
 

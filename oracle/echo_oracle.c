@@ -360,6 +360,9 @@ int eo_quantize_feedback(int bits, int group, int in_dtype, int state_dtype,
 /* Owner pass of rank `rank` over its own segment ([JP-1]: the owner    */
 /* sums in high precision, requantizes the sum and sends it to all;     */
 /* [JP-W]: quantize -> send -> decode -> add -> requantize).            */
+/* qpass (optional, length n) counts quantizer passes per element;      */
+/* acc_out (optional, one float per element of the segment) receives    */
+/* the fp32 sum before requantization.                                  */
 /* ------------------------------------------------------------------ */
 
 int eo_owner_reduce_requant(int bits, int group, int in_dtype, int state_dtype,
@@ -369,7 +372,7 @@ int eo_owner_reduce_requant(int bits, int group, int in_dtype, int state_dtype,
                             const uint8_t* const* in_codes,
                             const uint32_t* const* in_params,
                             uint8_t* out_codes, uint32_t* out_params,
-                            uint32_t* qpass)
+                            uint32_t* qpass, float* acc_out)
 {
     int rc = eo_check_common(bits, group, P, n);
     if (rc) return rc;
@@ -397,6 +400,7 @@ int eo_owner_reduce_requant(int bits, int group, int in_dtype, int state_dtype,
                 a = (p == 0) ? term : a + term;
             }
             acc[i] = a;
+            if (acc_out) acc_out[k] = a;   /* the fp32 sum, for tests that check it */
         }
         uint16_t sh, zh;
         eo_quantize_group(acc, glen, bits, q, &sh, &zh, deq);

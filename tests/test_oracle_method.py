@@ -138,6 +138,76 @@ def test_residuals_sum_to_negated_injected_error(P, bits, out_dtype):
     assert np.abs(e).max() > 100 * tol.max()        # the identity is not trivially satisfied
 
 
+# --------------------------------------------------------------- the owner's fp32 sum
+def exact_dequant(codes: np.ndarray, params: np.ndarray, bits: int, count: int) -> np.ndarray:
+    """code * step + zero for the first `count` elements of a payload, in
+    fp64 (exact: an 8-bit code times an fp16 step plus an fp16 zero needs at
+    most 51 significant bits), then rounded once to fp32 -- the value a
+    single-rounding fused multiply-add gives."""
+    if bits == 4:
+        q = np.empty(codes.size * 2, np.uint8)
+        q[0::2], q[1::2] = codes & 0xF, codes >> 4
+    else:
+        q = codes
+    q = q[:count].astype(np.float64)
+    grp = np.arange(count) // G
+    step = (params[grp] & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    zero = (params[grp] >> 16).astype(np.uint16).view(np.float16).astype(np.float64)
+    return (q * step + zero).astype(np.float32)
+
+
+@pytest.mark.parametrize("P", [2, 3, 5, 8, 16])
+@pytest.mark.parametrize("bits", [4, 8])
+def test_owner_sum_within_recursive_summation_bound(P, bits):
+    """The owner adds the P contributions in high precision ([JP]
+    'Echoの仕組み①'; binary32 here).  For m terms added one by one in
+    binary32, the computed sum s satisfies |s - exact| <= gamma_(m-1) *
+    sum|terms|, gamma_k = k u / (1 - k u), u = 2^-24 (the classical bound of
+    recursive summation).  Terms: the owner's own feedback-added input
+    x + eta (S + L) (random fp32 state, so it carries a full 24-bit
+    significand and most additions round) and the incoming payloads'
+    dequantized codes, both computed here independently of the oracle.
+    Magnitudes spread over four decades."""
+    import math
+    cfg = O.Config(bits=bits)
+    n = P * G * 6
+    rng = np.random.default_rng(70 + P + bits)
+    xs = [O.f32_to_bf16_bits((rng.standard_t(3, n) * 10.0 ** rng.uniform(-2, 2, n)).astype(np.float32))
+          for _ in range(P)]
+    Ss = [rng.normal(size=n).astype(np.float32) for _ in range(P)]
+    Ls = [(0.1 * rng.normal(size=n)).astype(np.float32) for _ in range(P)]
+    seg = O.segment_len(n, P, G)
+    # the owners' feedback-added inputs, before any pass touches the state
+    v_own = [(bf16_to_f64(xs[o]).astype(np.float32)
+              + np.float32(cfg.eta) * (Ss[o] + Ls[o]))[o * seg:(o + 1) * seg].astype(np.float64)
+             for o in range(P)]
+    sent = [[None if o == p else O.new_payload(cfg, seg) for o in range(P)] for p in range(P)]
+    for p in range(P):
+        O.quantize_feedback(cfg, P, p, xs[p], Ss[p], Ls[p],
+                            [None if o == p else sent[p][o][0] for o in range(P)],
+                            [None if o == p else sent[p][o][1] for o in range(P)])
+    u = 2.0 ** -24
+    gamma = (P - 1) * u / (1 - (P - 1) * u)
+    for o in (0, P - 1):
+        acc = np.zeros(seg, np.float32)
+        out = O.new_payload(cfg, seg)
+        O.owner_reduce_requant(cfg, P, o, xs[o], Ss[o], Ls[o],
+                               [None if p == o else sent[p][o][0] for p in range(P)],
+                               [None if p == o else sent[p][o][1] for p in range(P)],
+                               out[0], out[1], acc=acc)
+        terms = [v_own[o] if p == o else exact_dequant(sent[p][o][0], sent[p][o][1], bits, seg).astype(np.float64)
+                 for p in range(P)]
+        T = np.stack(terms)                                      # P x seg, rank order
+        exact = np.array([math.fsum(T[:, k]) for k in range(seg)])
+        bound = gamma * np.abs(T).sum(axis=0) * (1 + 1e-12)
+        err = np.abs(acc.astype(np.float64) - exact)
+        assert np.all(err <= bound), f"owner {o}: worst excess {np.max(err - bound)}"
+        assert np.count_nonzero(err) > seg // 4                 # additions do round
+        # a sum missing any one term lies far outside the bound
+        for p in range(P):
+            assert np.mean(np.abs(T[p]) > bound) > 0.9
+
+
 # --------------------------------------------------------------- chained calls
 def run_chain(cfg, P, n, sites, inputs):
     """Chain of `sites` calls with the state carried.  inputs(site) -> list of
