@@ -111,9 +111,13 @@ def test_entry_pass(P, groups, bits, in_dtype, state_dtype, group):
 @pytest.mark.parametrize("bits", [4, 8])
 @pytest.mark.parametrize("out_dtype", [B.ECHO_OUT_BF16, B.ECHO_OUT_F32])
 @pytest.mark.parametrize("in_dtype,state_dtype", TYPES)
-@pytest.mark.parametrize("P,groups", [(1, 9), (2, 37), (5, 8), (8, 13), (16, 2)])
+@pytest.mark.parametrize("P,groups", [(1, 9), (2, 37), (3, 11), (5, 8), (6, 5), (8, 13), (11, 3),
+                                      (16, 2)])
 @pytest.mark.parametrize("group", [128, 64, 32])
 def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype, group):
+    """Every slot count the owner kernel loads (P rounded up to 2, 4, 8, 16),
+    with unused slots (P = 3, 5, 6, 11), for the first, a middle and the last
+    rank."""
     banner(f"owner P={P} groups={groups} bits={bits} out={out_dtype} in={in_dtype} "
            f"state={state_dtype} group={group}")
     rng = np.random.default_rng(2000 * P + groups + bits + 10 * out_dtype + group)
@@ -122,7 +126,7 @@ def test_owner_pass(P, groups, bits, out_dtype, in_dtype, state_dtype, group):
     cfg = B.make_config(bits=bits, group=group, in_dtype=in_dtype, out_dtype=out_dtype,
                         state_dtype=state_dtype)
     ocfg = oracle_config(cfg)
-    for rank in sorted({0, P - 1}):
+    for rank in sorted({0, P // 2, P - 1}):
         xb, tdt = rand_input(rng, n, in_dtype, special=(rank == 0))
         s0, l0 = rand_state(rng, n, state_dtype), rand_state(rng, n, state_dtype, 0.2)
         inc = [None if p == rank else random_payload_host(rng, seg, bits, group) for p in range(P)]
