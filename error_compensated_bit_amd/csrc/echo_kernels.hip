@@ -25,9 +25,13 @@
 // contiguous.  The group min/max is a butterfly of DPP moves and, for runs of
 // 32 or more lanes, a ds_swizzle; a whole-wave group then combines its two
 // halves with a readlane of lanes 0 and 32.  Streamed arrays use nontemporal
-// loads and stores.  Launches are one-shot, one group per lane run, with
-// enough blocks to cover a segment: short-lived waves stream best here.  The
-// owner pass numbers its blocks XCD-contiguously.
+// loads and stores, except the owner pass's payload loads, where L2 should
+// serve the second half of a line to the neighbouring wave.  (Plain code
+// stores look faster for a kernel repeated alone, but they leave dirty lines
+// in the memory-side cache that the next kernel pays to write back.)
+// Launches are one-shot, one group per lane run, with enough blocks to cover
+// a segment: short-lived waves stream best here.  The owner pass numbers its
+// blocks XCD-contiguously.
 //
 // A message whose length is not a multiple of P*G has one partial group (in
 // its last non-empty segment); the main entry and owner kernels handle whole
