@@ -34,11 +34,16 @@ int64_t segment_len(int64_t n, int P, int group) {
   return (per + group - 1) / group * group;
 }
 
+// Longest message segment_len() is evaluated for: far beyond any valid shape
+// (16 ranks * 128 * 2^31 groups = 2^42), and small enough that its rounding
+// cannot overflow.
+constexpr int64_t kMaxLen = (int64_t)1 << 48;
+
 // P ranks, message of n >= 1 elements; a segment may hold at most 2^31 groups
 // (the kernels' 32-bit group index then cannot wrap).
 int check_shape(int P, int64_t n, int group) {
   if (P < 1 || P > ECHO_MAX_RANKS) return ECHO_ERR_ARG;
-  if (n <= 0) return ECHO_ERR_SHAPE;
+  if (n <= 0 || n > kMaxLen) return ECHO_ERR_SHAPE;
   if (segment_len(n, P, group) / group > ((int64_t)1 << 31)) return ECHO_ERR_SHAPE;
   return ECHO_OK;
 }
@@ -94,7 +99,7 @@ extern "C" {
 int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* stream) {
   if (!cfg) return ECHO_ERR_ARG;
   if (cfg->state_dtype != ECHO_STATE_F32 && cfg->state_dtype != ECHO_STATE_BF16) return ECHO_ERR_ARG;
-  if (n <= 0) return ECHO_ERR_ARG;
+  if (n <= 0 || n > kMaxLen) return ECHO_ERR_ARG;
   int rc;
   if ((rc = check_buf(state))) return rc;
   echo::run_zero(state, echo_state_bytes(n, cfg->state_dtype), static_cast<hipStream_t>(stream));
@@ -164,18 +169,20 @@ int echo_dequant_gather(const echo_config* cfg, int P, int64_t n, const echo_seg
 }
 
 size_t echo_codes_bytes(int64_t seg_len, int bits) {
-  if (seg_len <= 0 || (bits != 4 && bits != 8)) return 0;
+  if (seg_len <= 0 || seg_len > kMaxLen || (bits != 4 && bits != 8)) return 0;
   if (bits == 4 && seg_len % 2) return 0;
   return (size_t)seg_len * (size_t)bits / 8;
 }
 
 int64_t echo_segment_len(int64_t n, int P, int group) {
-  if (n <= 0 || P < 1 || P > ECHO_MAX_RANKS || (group != 32 && group != 64 && group != 128)) return 0;
+  if (n <= 0 || n > kMaxLen || P < 1 || P > ECHO_MAX_RANKS ||
+      (group != 32 && group != 64 && group != 128))
+    return 0;
   return segment_len(n, P, group);
 }
 
 size_t echo_state_bytes(int64_t n, int state_dtype) {
-  if (n <= 0) return 0;
+  if (n <= 0 || n > kMaxLen) return 0;
   if (state_dtype == ECHO_STATE_F32) return (size_t)n * 8;
   if (state_dtype == ECHO_STATE_BF16) return (size_t)n * 4;
   return 0;

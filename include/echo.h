@@ -70,7 +70,8 @@ extern "C" {
 /* return codes */
 #define ECHO_OK          0
 #define ECHO_ERR_ARG    -1   /* null pointer, unsupported or out-of-range parameter */
-#define ECHO_ERR_SHAPE  -2   /* n <= 0, or a segment of more than 2^31 groups */
+#define ECHO_ERR_SHAPE  -2   /* n <= 0, or a segment of more than 2^31 groups
+                                (every n > 2^48 is one) */
 #define ECHO_ERR_ALIGN  -3   /* a buffer pointer is not 16-byte aligned */
 #define ECHO_ERR_HIP    -4   /* the HIP runtime reported an error at launch */
 
@@ -109,7 +110,7 @@ typedef struct echo_seg {
  *   The feedback of [JP-2] carries error into later calls; a chain of calls
  *   starts from an empty state.  Implemented as a fill kernel (no memset
  *   node), so it may be captured in a HIP graph.
- *   Errors: ECHO_ERR_ARG (null cfg/pointer, n <= 0, bad state type),
+ *   Errors: ECHO_ERR_ARG (null cfg/pointer, n <= 0 or n > 2^48, bad state type),
  *   ECHO_ERR_ALIGN, ECHO_ERR_HIP.
  */
 int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* stream);

@@ -43,6 +43,8 @@ def test_segment_len_agrees_with_the_oracle():
     assert B.echo_segment_len(0, 2, 128) == 0
     assert B.echo_segment_len(100, 17, 128) == 0
     assert B.echo_segment_len(100, 2, 48) == 0
+    assert B.echo_segment_len((1 << 63) - 1, 2, 128) == 0      # no overflow in the rounding
+    assert B.echo_segment_len(1 << 42, 16, 128) == 1 << 38
 
 
 def test_state_sizes():
@@ -100,6 +102,10 @@ def cfg(**kw):
     (lambda L: L.echo_dequant_gather(cfg(), 2, 0, SEGS, A, None), B.ECHO_ERR_SHAPE),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 2 * 128 * ((1 << 31) + 1), A, A, SEGS, None),
      B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, (1 << 63) - 1, A, A, SEGS, None),
+     B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_dequant_gather(cfg(), 16, (1 << 62) + 7, SEGS, A, None), B.ECHO_ERR_SHAPE),
+    (lambda L: L.echo_state_reset(cfg(), A, (1 << 62), None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, None, A, SEGS, None), B.ECHO_ERR_ARG),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A + 8, A, SEGS, None), B.ECHO_ERR_ALIGN),
     (lambda L: L.echo_quantize_feedback(cfg(), 2, 0, 256, A, A + 4, SEGS, None), B.ECHO_ERR_ALIGN),
