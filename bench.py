@@ -199,6 +199,23 @@ def copy_calibration(nbytes: int):
     log(f"copy calibration: {nbytes} bytes read and written per launch, 3 launches")
 
 
+def host_cpu() -> str:
+    """The host's CPU model and logical CPU count, for the baseline's record."""
+    model = "unknown CPU"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return f"{model}, {os.cpu_count()} logical CPUs ({usable} usable by this process)"
+
+
 def cpu_threads(P: int) -> int:
     """Threads for the parallel oracle run: one per simulated rank, within the
     cores this process may use (and at most 16, the host share of one GPU)."""
@@ -292,7 +309,7 @@ def cpu_baseline(cfg, w, xs_dev, frac_den: int):
                       f"entry, owner and gather calls on {T} threads, {t_par:.2f} s wall for "
                       f"{P} shares. Single-threaded: one share {t_share:.2f} s (entry "
                       f"{t_entry / P:.2f} + owner {t_owner / P:.2f} + gather {t_gather:.2f}) "
-                      f"= {single:.4f} GB/s. Scalar C oracle."}
+                      f"= {single:.4f} GB/s. Scalar C oracle. Host: {host_cpu()}."}
 
 
 def main():
