@@ -123,7 +123,7 @@ def _kernel_key(name: str) -> str:
 
 def summarize_profiles(d: str, workload: str = "msg1gib_p8", copy_bytes: int = 1 << 30):
     """Reduce the rocprofv3 CSVs of PROFILE_COMMANDS (run from the repository
-    root on the GPU machine, DIR = their output folder) to profiles/."""
+    root on the machine with the GPU, DIR = their output folder) to profiles/."""
     import csv
     from collections import defaultdict
     from error_compensated_bit_amd import binding as B
