@@ -88,9 +88,7 @@ LaunchArgs base_args(const echo_config* c, int P, int rank, int64_t n) {
   return a;
 }
 
-int launched() {
-  return hipGetLastError() == hipSuccess ? ECHO_OK : ECHO_ERR_HIP;
-}
+int launched(hipError_t e) { return e == hipSuccess ? ECHO_OK : ECHO_ERR_HIP; }
 
 }  // namespace
 
@@ -102,8 +100,8 @@ int echo_state_reset(const echo_config* cfg, void* state, int64_t n, void* strea
   if (n <= 0 || n > kMaxLen) return ECHO_ERR_ARG;
   int rc;
   if ((rc = check_buf(state))) return rc;
-  echo::run_zero(state, echo_state_bytes(n, cfg->state_dtype), static_cast<hipStream_t>(stream));
-  return launched();
+  return launched(echo::run_zero(state, echo_state_bytes(n, cfg->state_dtype),
+                                 static_cast<hipStream_t>(stream)));
 }
 
 int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n, const void* x,
@@ -123,8 +121,7 @@ int echo_quantize_feedback(const echo_config* cfg, int P, int rank, int64_t n, c
   if (P == 1) return ECHO_OK;  // nothing is sent when a rank owns the whole message
   a.x = x;
   a.state = state;
-  echo::run_quant_feedback(a, static_cast<hipStream_t>(stream));
-  return launched();
+  return launched(echo::run_quant_feedback(a, static_cast<hipStream_t>(stream)));
 }
 
 int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n, const void* x,
@@ -147,8 +144,7 @@ int echo_owner_reduce_requant(const echo_config* cfg, int P, int rank, int64_t n
   a.state = state;
   a.out_codes = out->codes;
   a.out_params = out->params;
-  echo::run_owner_reduce_requant(a, static_cast<hipStream_t>(stream));
-  return launched();
+  return launched(echo::run_owner_reduce_requant(a, static_cast<hipStream_t>(stream)));
 }
 
 int echo_dequant_gather(const echo_config* cfg, int P, int64_t n, const echo_seg* in, void* out,
@@ -164,8 +160,7 @@ int echo_dequant_gather(const echo_config* cfg, int P, int64_t n, const echo_seg
     a.segs.params[p] = in[p].params;
   }
   a.out = out;
-  echo::run_dequant_gather(a, static_cast<hipStream_t>(stream));
-  return launched();
+  return launched(echo::run_dequant_gather(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t echo_codes_bytes(int64_t seg_len, int bits) {

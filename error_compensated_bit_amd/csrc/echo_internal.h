@@ -43,9 +43,10 @@ struct LaunchArgs {
   Coef coef;
 };
 
-void run_quant_feedback(const LaunchArgs& a, hipStream_t st);
-void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st);
-void run_dequant_gather(const LaunchArgs& a, hipStream_t st);
-void run_zero(void* p, uint64_t bytes, hipStream_t st);
+// Each returns the first launch error (hipSuccess when every launch went out).
+hipError_t run_quant_feedback(const LaunchArgs& a, hipStream_t st);
+hipError_t run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st);
+hipError_t run_dequant_gather(const LaunchArgs& a, hipStream_t st);
+hipError_t run_zero(void* p, uint64_t bytes, hipStream_t st);
 
 }  // namespace echo

@@ -736,20 +736,35 @@ unsigned blocks_for(uint64_t groups, uint64_t groups_per_block) {
 
 }  // namespace
 
+// Launch `kernel` with its own status: hipLaunchKernel returns the launch's
+// error, so no pending error of the caller's is read or cleared.  The
+// arguments convert to the kernel's parameter types.
+template <typename T>
+struct Same {
+  using type = T;
+};
+template <typename... Params>
+hipError_t launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t st,
+                  typename Same<Params>::type... args) {
+  void* ptrs[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, st);
+}
+
 template <int BITS, int IN_T, int ST_T, int G, bool NT, bool XCD>
-void launch_k1(const LaunchArgs& a, hipStream_t st) {
+hipError_t launch_k1(const LaunchArgs& a, hipStream_t st) {
   const uint64_t groups = a.seg_len / G;
   const unsigned ny = (unsigned)(a.P - 1);
   dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock), ny);
-  hipLaunchKernelGGL((k_quant_feedback<BITS, IN_T, ST_T, G, NT, XCD>), grid, dim3(kThreads), 0,
-                     st, static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
-                     full_groups(a.n, a.seg_len, G), a.seg_len, a.coef);
+  hipError_t e = launch(k_quant_feedback<BITS, IN_T, ST_T, G, NT, XCD>, grid, dim3(kThreads), st,
+                        static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
+                        full_groups(a.n, a.seg_len, G), a.seg_len, a.coef);
   const Tail t = tail_of(a.n, a.seg_len, G);
-  if (t.valid && (int)t.p != a.rank)
-    hipLaunchKernelGGL((k_quant_feedback_tail<BITS, IN_T, ST_T, G>), dim3(1),
-                       dim3(GroupMap<ST_T, G>::kLanes), 0, st, static_cast<const uint16_t*>(a.x),
-                       a.state, static_cast<uint8_t*>(a.segs.codes[t.p]), a.segs.params[t.p],
-                       (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
+  if (e == hipSuccess && t.valid && (int)t.p != a.rank)
+    e = launch(k_quant_feedback_tail<BITS, IN_T, ST_T, G>, dim3(1), dim3(GroupMap<ST_T, G>::kLanes),
+               st, static_cast<const uint16_t*>(a.x), a.state,
+               static_cast<uint8_t*>(a.segs.codes[t.p]), a.segs.params[t.p],
+               (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
+  return e;
 }
 
 // The incoming table as the owner pass reads it: the owner's own slot, which
@@ -771,33 +786,36 @@ SegTable owner_table(const LaunchArgs& a) {
 }
 
 template <int BITS, int IN_T, int ST_T, int OUT_T, int G, int NP, bool NT, bool NTP, bool XCD>
-void launch_k2(const LaunchArgs& a, hipStream_t st) {
+hipError_t launch_k2(const LaunchArgs& a, hipStream_t st) {
   const uint64_t groups = a.seg_len / G;
   const SegTable in = owner_table(a);
   dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock));
-  hipLaunchKernelGGL((k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, XCD>), grid,
-                     dim3(kThreads), 0, st, static_cast<const uint16_t*>(a.x), a.state, in,
-                     a.P, a.rank, full_groups(a.n, a.seg_len, G), a.seg_len,
-                     static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
+  hipError_t e = launch(k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, XCD>, grid,
+                        dim3(kThreads), st, static_cast<const uint16_t*>(a.x), a.state, in, a.P,
+                        a.rank, full_groups(a.n, a.seg_len, G), a.seg_len,
+                        static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
   const Tail t = tail_of(a.n, a.seg_len, G);
-  if (t.valid && (int)t.p == a.rank)
-    hipLaunchKernelGGL((k_owner_reduce_requant_tail<BITS, IN_T, ST_T, OUT_T, G>), dim3(1),
-                       dim3(GroupMap<ST_T, G>::kLanes), 0, st, static_cast<const uint16_t*>(a.x),
-                       a.state, in, a.P, a.rank, static_cast<uint8_t*>(a.out_codes),
-                       a.out_params, (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
+  if (e == hipSuccess && t.valid && (int)t.p == a.rank)
+    e = launch(k_owner_reduce_requant_tail<BITS, IN_T, ST_T, OUT_T, G>, dim3(1),
+               dim3(GroupMap<ST_T, G>::kLanes), st, static_cast<const uint16_t*>(a.x), a.state, in,
+               a.P, a.rank, static_cast<uint8_t*>(a.out_codes), a.out_params,
+               (uint64_t)t.p * a.seg_len, t.g, t.valid, a.coef);
+  return e;
 }
 
 template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
-void launch_k3(const LaunchArgs& a, hipStream_t st) {
+hipError_t launch_k3(const LaunchArgs& a, hipStream_t st) {
   constexpr uint32_t tile = gather_groups_per_block<OUT_T, G, CH>();
   const FullGroups fg = full_groups(a.n, a.seg_len, G);
   const Tail t = tail_of(a.n, a.seg_len, G);
+  hipError_t e = hipSuccess;
   if (fg.all / tile > 0)
-    hipLaunchKernelGGL((k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>), dim3(fg.all / tile, a.P),
-                       dim3(kThreads), 0, st, a.segs, fg, a.seg_len, a.out);
-  if (fg.all % tile || fg.in_last % tile || t.valid)
-    hipLaunchKernelGGL((k_dequant_gather_tail<BITS, OUT_T, G, CH>), dim3(1, a.P), dim3(kThreads), 0,
-                       st, a.segs, fg, a.n, a.seg_len, a.out);
+    e = launch(k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>, dim3(fg.all / tile, a.P),
+               dim3(kThreads), st, a.segs, fg, a.seg_len, a.out);
+  if (e == hipSuccess && (fg.all % tile || fg.in_last % tile || t.valid))
+    e = launch(k_dequant_gather_tail<BITS, OUT_T, G, CH>, dim3(1, a.P), dim3(kThreads), st, a.segs,
+               fg, a.n, a.seg_len, a.out);
+  return e;
 }
 
 // Nontemporal loads and stores for every streamed array, except the owner
@@ -839,34 +857,39 @@ void with_slots(int P, F&& f) {
   else f(IC<kMaxRanks>{});
 }
 
-void run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
+hipError_t run_quant_feedback(const LaunchArgs& a, hipStream_t st) {
+  hipError_t e = hipSuccess;
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
     with_state(a.state_dtype, [&](auto S) {
-      launch_k1<B(), I(), S(), G(), kNT, kXcdOrderEntry>(a, st);
+      e = launch_k1<B(), I(), S(), G(), kNT, kXcdOrderEntry>(a, st);
     }); }); }); });
+  return e;
 }
 
-void run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
+hipError_t run_owner_reduce_requant(const LaunchArgs& a, hipStream_t st) {
+  hipError_t e = hipSuccess;
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_in(a.in_dtype, [&](auto I) {
     with_state(a.state_dtype, [&](auto S) { with_out(a.out_dtype, [&](auto O) {
       with_slots(a.P, [&](auto NP) {
-        launch_k2<B(), I(), S(), O(), G(), NP(), kNT, kNTOwnerPayload, kXcdOrderOwner>(a, st);
+        e = launch_k2<B(), I(), S(), O(), G(), NP(), kNT, kNTOwnerPayload, kXcdOrderOwner>(a, st);
       }); }); }); }); }); });
+  return e;
 }
 
-void run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
+hipError_t run_dequant_gather(const LaunchArgs& a, hipStream_t st) {
+  hipError_t e = hipSuccess;
   with_group(a.group, [&](auto G) { with_bits(a.bits, [&](auto B) { with_out(a.out_dtype, [&](auto O) {
-    launch_k3<B(), O(), G(), kGatherChunks, kNT, kNT>(a, st);
+    e = launch_k3<B(), O(), G(), kGatherChunks, kNT, kNT>(a, st);
   }); }); });
+  return e;
 }
 
-void run_zero(void* p, uint64_t bytes, hipStream_t st) {
+hipError_t run_zero(void* p, uint64_t bytes, hipStream_t st) {
   const uint64_t n16 = bytes / 16;
   uint64_t blocks = (n16 + kThreads - 1) / kThreads;
   if (blocks > kZeroGridCap) blocks = kZeroGridCap;
   if (blocks == 0) blocks = 1;
-  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(kThreads), 0, st,
-                     static_cast<uint8_t*>(p), bytes);
+  return launch(k_zero, dim3((unsigned)blocks), dim3(kThreads), st, static_cast<uint8_t*>(p), bytes);
 }
 
 }  // namespace echo
