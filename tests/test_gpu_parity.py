@@ -258,6 +258,27 @@ def test_runs_on_the_callers_stream():
     assert torch.equal(r1.out, r2.out)
 
 
+def test_a_pending_error_of_the_caller_is_left_alone():
+    """A HIP error the caller left pending (here a failed allocation, which
+    touches no memory) neither fails a library call nor is cleared by it:
+    each call checks its own launches' status."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    cfg = B.make_config()
+    n = 4096
+    state = torch.full((2 * n,), 7.0, device=DEV)
+    torch.cuda.synchronize()
+    hip.hipGetLastError()                                   # start from a clean slate
+    ptr = ctypes.c_void_p()
+    rc = hip.hipMalloc(ctypes.byref(ptr), ctypes.c_size_t(1 << 62))
+    assert rc != 0
+    B.echo_state_reset(cfg, state, n)                       # must not raise
+    assert hip.hipGetLastError() == rc                      # still pending, then cleared
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(state).item() == 0
+
+
 def test_invalid_arguments_raise():
     cfg = B.make_config()
     x = torch.zeros(1024, dtype=torch.bfloat16, device=DEV)
