@@ -43,7 +43,7 @@ def draw_cases(count: int, seed: int):
     return cases
 
 
-CASES = draw_cases(96, 20261203)
+CASES = draw_cases(256, 20261203)
 
 
 def make_inputs(rng, n, in_dtype, scale):
