@@ -258,6 +258,41 @@ def test_runs_on_the_callers_stream():
     assert torch.equal(r1.out, r2.out)
 
 
+def test_concurrent_host_threads_on_separate_streams():
+    """The library keeps no state between calls: four host threads, each
+    driving its own ranks on its own stream, produce what sequential calls
+    produce (the binding releases the interpreter lock during each call)."""
+    from concurrent.futures import ThreadPoolExecutor
+    P, seg = 4, 24 * G
+    n = P * seg
+    cfg = B.make_config()
+    rng = np.random.default_rng(11)
+    inputs = [[device_bits16(rand_input(rng, n, B.ECHO_IN_BF16)[0], torch.bfloat16, DEV)
+               for _ in range(P)] for _ in range(4)]
+    ref = []
+    for xs in inputs:
+        r = sim.alloc_ranks(cfg, P, n, DEV)
+        for _ in range(3):
+            sim.allreduce(cfg, r, xs)
+        ref.append((r.out.clone(), [st.clone() for st in r.state]))
+    torch.cuda.synchronize()
+    ranks = [sim.alloc_ranks(cfg, P, n, DEV) for _ in inputs]
+    streams = [torch.cuda.Stream() for _ in inputs]
+    torch.cuda.synchronize()
+
+    def work(i):
+        for _ in range(3):
+            sim.allreduce(cfg, ranks[i], inputs[i], stream=streams[i])
+
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        list(pool.map(work, range(len(inputs))))
+    torch.cuda.synchronize()
+    for i, (out, states) in enumerate(ref):
+        assert torch.equal(ranks[i].out, out), f"thread {i} output"
+        for p in range(P):
+            assert torch.equal(ranks[i].state[p], states[p]), f"thread {i} rank {p} state"
+
+
 def test_a_pending_error_of_the_caller_is_left_alone():
     """A HIP error the caller left pending (here a failed allocation, which
     touches no memory) neither fails a library call nor is cleared by it:
