@@ -449,7 +449,8 @@ def main():
                    "eta": cfg.eta, "beta_short": cfg.beta_short, "beta_long": cfg.beta_long,
                    "mix_long": round(cfg.mix_long, 6),
                    "algorithmic_bytes_per_step": int(alg_total),
-                   "input_sha256": input_digests(xs)},
+                   "input_sha256": input_digests(xs),
+                   "kernel_source_digest": kernel_source_digest()},
         "kernel_ms": {k: round(v, 5) for k, v in k_ms.items()},
         "ms_per_step_eager": round(ms_eager, 5),
         "ms_step_events": {"median": round(statistics.median(ev_steps), 5),

@@ -258,6 +258,34 @@ def test_runs_on_the_callers_stream():
     assert torch.equal(r1.out, r2.out)
 
 
+def test_reset_recovers_a_corrupted_state():
+    """NaN and Inf in the error state are outside the contract and make the
+    call's results undefined; echo_state_reset then restores a clean chain:
+    two calls after the reset equal two calls from freshly allocated ranks."""
+    P, seg = 4, 12 * G
+    n = P * seg
+    cfg = B.make_config()
+    rng = np.random.default_rng(13)
+    xs = [device_bits16(rand_input(rng, n, B.ECHO_IN_BF16)[0], torch.bfloat16, DEV) for _ in range(P)]
+    fresh = sim.alloc_ranks(cfg, P, n, DEV)
+    for _ in range(2):
+        sim.allreduce(cfg, fresh, xs)
+    r = sim.alloc_ranks(cfg, P, n, DEV)
+    for st in r.state:
+        st[0::7] = float("nan")
+        st[3::11] = float("inf")
+        st[5::13] = -float("inf")
+    sim.allreduce(cfg, r, xs)                 # undefined results, but every kernel finishes
+    for st in r.state:
+        B.echo_state_reset(cfg, st, n)
+    for _ in range(2):
+        sim.allreduce(cfg, r, xs)
+    torch.cuda.synchronize()
+    assert torch.equal(r.out, fresh.out)
+    for p in range(P):
+        assert torch.equal(r.state[p], fresh.state[p])
+
+
 def test_concurrent_host_threads_on_separate_streams():
     """The library keeps no state between calls: four host threads, each
     driving its own ranks on its own stream, produce what sequential calls
