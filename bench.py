@@ -13,7 +13,8 @@ input bytes per second), the metric the method is quoted on; hbm_frac is
 the algorithmic bytes per step over MI355X's 8 TB/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--site S]
-                       [--state f32|bf16] [--graph]
+                       [--state f32|bf16] [--group G] [--graph]
+       python bench.py --n N [--ranks P] [--bits 4|8] ...   (any message size)
        python bench.py --copy-calibration BYTES     (plain copy for PMC scaling)
        python bench.py --summarize-profiles DIR     (rocprofv3 CSVs -> profiles/)
 """
@@ -318,6 +319,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="msg1gib_p8")
+    ap.add_argument("--n", type=int, default=0,
+                    help="instead of a named workload: a message of N bf16 elements per rank, "
+                         "iid N(0,1), one call (N a multiple of ranks * group)")
+    ap.add_argument("--ranks", type=int, default=8, help="simulated ranks P with --n")
+    ap.add_argument("--bits", type=int, choices=(4, 8), default=4, help="code width with --n")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--site", type=int, default=0,
                     help="call of a chained workload whose inputs and width are used")
@@ -348,10 +354,17 @@ def main():
 
     from error_compensated_bit_amd import binding as B
     from error_compensated_bit_amd import sim
-    from error_compensated_bit_amd.inputs import WORKLOADS, make_x
+    from error_compensated_bit_amd.inputs import WORKLOADS, Workload, make_x
 
     B.load_library()
-    w = WORKLOADS[args.workload]
+    if args.n:
+        if args.n % (args.ranks * args.group) or not 1 <= args.ranks <= B.ECHO_MAX_RANKS:
+            sys.exit(f"--n must be a positive multiple of ranks * group ({args.ranks} * {args.group})")
+        w = Workload(f"custom_p{args.ranks}_n{args.n}", 90, args.ranks, (args.n,), "normal", 1,
+                     (1, args.bits, args.bits),
+                     description=f"{args.n} bf16 elements per rank, P={args.ranks}, iid N(0,1)")
+    else:
+        w = WORKLOADS[args.workload]
     P, n = w.P, w.n
     bits = w.bits(args.site)
     sdt = B.ECHO_STATE_F32 if args.state == "f32" else B.ECHO_STATE_BF16
