@@ -258,6 +258,46 @@ def test_runs_on_the_callers_stream():
     assert torch.equal(r1.out, r2.out)
 
 
+@pytest.mark.parametrize("bits,in_dtype", [(4, B.ECHO_IN_BF16), (8, B.ECHO_IN_F16)])
+@pytest.mark.parametrize("group", [128, 32])
+def test_exact_ties_round_to_even(bits, in_dtype, group):
+    """Groups built so that most elements sit exactly halfway between two
+    codes: min 0 and max qmax * s with s a power of two, the rest at
+    (k + 1/2) * s.  Codes must round half to even, as on the CPU."""
+    P, groups = 2, 40
+    seg = groups * group
+    n = P * seg
+    qmax = (1 << bits) - 1
+    s = 2.0 if bits == 4 else 0.5
+    rng = np.random.default_rng(17 + bits + group)
+    v = ((rng.integers(0, qmax, size=n) + 0.5) * s).astype(np.float32)
+    v[0::group] = 0.0
+    v[1::group] = qmax * s
+    xb = O.f32_to_f16_bits(v) if in_dtype == B.ECHO_IN_F16 else O.f32_to_bf16_bits(v)
+    tdt = torch.float16 if in_dtype == B.ECHO_IN_F16 else torch.bfloat16
+    back = (xb.astype(np.uint32) << 16).view(np.float32) if in_dtype == B.ECHO_IN_BF16 else \
+        xb.view(np.float16).astype(np.float32)
+    assert np.array_equal(back, v)                          # the ties survive the 16-bit input
+    cfg = B.make_config(bits=bits, group=group, in_dtype=in_dtype)
+    ocfg = oracle_config(cfg)
+    x = device_bits16(xb, tdt, DEV)
+    state = torch.zeros(2 * n, device=DEV)
+    out = [None, B.alloc_payload(seg, bits, DEV, group=group)]
+    B.echo_quantize_feedback(cfg, P, 0, n, x, state, out)
+    torch.cuda.synchronize()
+    oc = [None, np.zeros(seg * bits // 8, np.uint8)]
+    op = [None, np.zeros(groups, np.uint32)]
+    O.quantize_feedback(ocfg, P, 0, xb, np.zeros(n, np.float32), np.zeros(n, np.float32), oc, op)
+    assert_bits_equal(host(out[1].codes), oc[1], "codes")
+    assert_bits_equal(host(out[1].params), op[1], "params")
+    codes = oc[1] if bits == 8 else np.stack([oc[1] & 15, oc[1] >> 4], axis=1).reshape(-1)
+    k = np.rint(v[seg:] / s - 0.5).astype(np.int64)          # the tie lies between k and k + 1
+    tie = np.ones(seg, bool)
+    tie[0::group] = tie[1::group] = False
+    assert np.all(codes[tie] % 2 == 0)
+    assert np.all(codes[tie] == np.where(k[tie] % 2 == 0, k[tie], k[tie] + 1))
+
+
 def test_reset_recovers_a_corrupted_state():
     """NaN and Inf in the error state are outside the contract and make the
     call's results undefined; echo_state_reset then restores a clean chain:
