@@ -298,6 +298,53 @@ def test_exact_ties_round_to_even(bits, in_dtype, group):
     assert np.all(codes[tie] == np.where(k[tie] % 2 == 0, k[tie], k[tie] + 1))
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_fp16_parameter_ties(bits):
+    """Groups whose minimum lies exactly halfway between two fp16 values, and
+    whose span / qmax is again exactly halfway between two fp16 values: both
+    the zero point and the step must round half to even, as on the CPU.  The
+    feedback term carries the values (x = 0, S = v, L = 0, gain 1), so any
+    binary32 value can be placed in the group exactly."""
+    P, groups, group = 2, 64, 128
+    seg = groups * group
+    n = P * seg
+    qmax = (1 << bits) - 1
+    rng = np.random.default_rng(23 + bits)
+    h = rng.integers(0x0400, 0x5000, size=groups).astype(np.uint16)   # normal fp16, below 32
+    lo = h.view(np.float16).astype(np.float32)
+    hi = (h + 1).view(np.float16).astype(np.float32)
+    mn = (lo + hi) / 2                                      # exact fp32 midpoints
+    zf = mn.astype(np.float16).astype(np.float32)           # round half to even
+    hs = rng.integers(0x2000, 0x4400, size=groups).astype(np.uint16)
+    m = (hs.view(np.float16).astype(np.float32) + (hs + 1).view(np.float16).astype(np.float32)) / 2
+    mx = zf + m * np.float32(qmax)
+    assert np.all((mx - zf) / np.float32(qmax) == m)       # the quotient is the midpoint itself
+    v = np.empty((groups, group), np.float32)
+    for gi in range(groups):
+        v[gi] = rng.uniform(mn[gi], mx[gi], size=group).astype(np.float32)
+        v[gi, 0], v[gi, 1] = mn[gi], mx[gi]
+        v[gi] = np.clip(v[gi], mn[gi], mx[gi])
+    S = np.zeros(n, np.float32)
+    S[seg:] = v.reshape(-1)
+    cfg = B.make_config(bits=bits, group=group)
+    ocfg = oracle_config(cfg)
+    xb = np.zeros(n, np.uint16)
+    x = device_bits16(xb, torch.bfloat16, DEV)
+    state = state_dev(interleave(S, np.zeros(n, np.float32)))
+    out = [None, B.alloc_payload(seg, bits, DEV, group=group)]
+    B.echo_quantize_feedback(cfg, P, 0, n, x, state, out)
+    torch.cuda.synchronize()
+    oc = [None, np.zeros(seg * bits // 8, np.uint8)]
+    op = [None, np.zeros(groups, np.uint32)]
+    so, lo_ = S.copy(), np.zeros(n, np.float32)
+    O.quantize_feedback(ocfg, P, 0, xb, so, lo_, oc, op)
+    assert_bits_equal(host(out[1].params), op[1], "params")
+    assert_bits_equal(host(out[1].codes), oc[1], "codes")
+    cmp_state(state, so, lo_, "state")
+    step_bits, zero_bits = op[1] & 0xFFFF, op[1] >> 16
+    assert np.all(zero_bits & 1 == 0) and np.all(step_bits & 1 == 0)   # ties went to even
+
+
 def test_reset_recovers_a_corrupted_state():
     """NaN and Inf in the error state are outside the contract and make the
     call's results undefined; echo_state_reset then restores a clean chain:
