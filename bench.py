@@ -61,12 +61,15 @@ def algorithmic_bytes(P: int, n: int, bits: int, state_bytes: int, in_bytes=2, o
 
 def kernel_source_digest() -> str:
     """Digest of what determines the kernels' code: their source, the header
-    they include and the compiler flags (not the argument-checking layer)."""
+    they include and the compiler flags (not the argument-checking layer).
+    Paths in the flags are taken relative to the repository, so the digest
+    does not depend on where the repository sits."""
     from error_compensated_bit_amd import build as eb
     h = hashlib.sha256()
     for f in (os.path.join(eb.CSRC, "echo_kernels.hip"), os.path.join(eb.CSRC, "echo_internal.h")):
         h.update(open(f, "rb").read())
-    h.update(" ".join(eb.hipcc_flags()).encode())
+    flags = [os.path.relpath(f, HERE) if os.path.isabs(f) else f for f in eb.hipcc_flags()]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
