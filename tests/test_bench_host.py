@@ -35,3 +35,10 @@ def test_kernel_digest_does_not_depend_on_the_repository_location(tmp_path):
     out = subprocess.run([sys.executable, "-c", "import bench; print(bench.kernel_source_digest())"],
                          cwd=tmp_path, capture_output=True, text=True, check=True)
     assert out.stdout.strip() == bench.kernel_source_digest()
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60, cwd=ROOT)
+    assert r.returncode != 0
+    assert "--gpus 1" in r.stderr
