@@ -87,15 +87,22 @@ def input_digests(xs):
     return out
 
 
-def traffic_from_profile(workload: str, kernel: str):
+# The launch configuration the profile commands measure (bench.py's defaults).
+PROFILED_CONFIG = {"state": "f32", "group": 128, "site": 0, "rank": 0}
+
+
+def traffic_from_profile(workload: str, kernel: str, config: dict):
     """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE,
     scaled by the same counters on a plain copy of known size; None when no
-    summary exists or the kernels changed since it was taken."""
+    summary exists, the kernels changed since it was taken, or this run's
+    configuration is not the one profiled."""
     path = os.path.join(HERE, "profiles", f"pmc_{workload}.json")
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
     if d.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    if d.get("config", PROFILED_CONFIG) != config:
         return None
     k = d["kernels"].get(kernel)
     c = d["copy_calibration"]
@@ -152,6 +159,7 @@ def summarize_profiles(d: str, workload: str = "msg1gib_p8", copy_bytes: int = 1
     alg = algorithmic_bytes(w.P, w.n, w.bits(0), 4)
     out = {
         "workload": workload,
+        "config": PROFILED_CONFIG,
         "kernel_source_digest": kernel_source_digest(),
         "commands": PROFILE_COMMANDS,
         "copy_calibration": {"kernel": copy_key, "bytes_read": copy_bytes, "bytes_written": copy_bytes,
@@ -443,7 +451,8 @@ def main():
 
     dom = max(KERNELS, key=lambda k: alg[k])
     achieved = alg[dom] / k_ms[dom] / 1e6
-    traffic = traffic_from_profile(w.name, dom)
+    traffic = traffic_from_profile(w.name, dom, {"state": args.state, "group": args.group,
+                                                 "site": args.site, "rank": args.rank})
     value = 2.0 * n / (ms_per_step * 1e-3) / 1e9
     line = {
         "metric": METRIC,

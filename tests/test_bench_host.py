@@ -42,3 +42,17 @@ def test_bench_refuses_more_than_one_gpu():
                        capture_output=True, text=True, timeout=60, cwd=ROOT)
     assert r.returncode != 0
     assert "--gpus 1" in r.stderr
+
+
+def test_traffic_is_reported_only_for_the_profiled_configuration():
+    """profiles/ holds counters for the default launch (fp32 state, group
+    128, rank 0); another configuration of the same workload reports none."""
+    cfg = dict(bench.PROFILED_CONFIG)
+    t = bench.traffic_from_profile("msg1gib_p8", "k_quant_feedback", cfg)
+    if t is None:
+        import pytest
+        pytest.skip("no profile for the current kernel source")
+    alg = bench.algorithmic_bytes(8, 536870912, 4, 4)["k_quant_feedback"]
+    assert 0.99 < t / alg < 1.05
+    for change in ({"state": "bf16"}, {"group": 64}, {"rank": 3}, {"site": 5}):
+        assert bench.traffic_from_profile("msg1gib_p8", "k_quant_feedback", {**cfg, **change}) is None
