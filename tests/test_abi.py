@@ -135,3 +135,13 @@ def test_invalid_arguments_return_codes(call, code):
 def test_error_strings():
     for c in (0, -1, -2, -3, -4, 99):
         assert isinstance(B.error_string(c), str) and B.error_string(c)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library the binding raises, naming the
+    file and how to build it."""
+    from error_compensated_bit_amd import binding
+    monkeypatch.setattr(binding, "_LIB", None)
+    monkeypatch.setattr(binding, "library_path", lambda: str(tmp_path / "libecho_amd.so"))
+    with pytest.raises(RuntimeError, match="build"):
+        binding.load_library()
