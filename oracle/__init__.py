@@ -154,8 +154,13 @@ def quantize_group(v: np.ndarray, bits: int):
 
 
 # ---------------------------------------------------------------- the four calls
-def state_reset(S: np.ndarray, L: np.ndarray, cfg: Config = Config()):
-    _check(lib().eo_state_reset(_ptr(S), _ptr(L), cfg.state_dtype, S.size), "state_reset")
+def state_reset(S: np.ndarray, L: np.ndarray, cfg: Config = Config(), n: int | None = None):
+    """Empty both memories of the first n elements (default: all of S and L);
+    S and L hold float32 (fp32 state) or uint16 bfloat16 bits (bf16 state)."""
+    n = S.size if n is None else n
+    assert S.dtype == state_np_dtype(cfg) and L.dtype == S.dtype
+    assert 0 <= n <= min(S.size, L.size)
+    _check(lib().eo_state_reset(_ptr(S), _ptr(L), cfg.state_dtype, n), "state_reset")
 
 
 def quantize_feedback(cfg: Config, P: int, rank: int, x: np.ndarray, S: np.ndarray,

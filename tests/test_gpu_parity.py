@@ -184,15 +184,27 @@ def test_dequant_gather(P, groups, bits, out_dtype, group):
 @pytest.mark.parametrize("state_dtype", [B.ECHO_STATE_F32, B.ECHO_STATE_BF16])
 @pytest.mark.parametrize("n", [1, 7, 8, 129, 4096, 1000003])
 def test_state_reset(n, state_dtype):
+    """The reset of a state holding garbage (NaN, Inf, -0, huge values)
+    against the oracle's reset of the same garbage, interleaved into the
+    device layout; the 16 elements past the 2n state words are sentinels."""
     cfg = B.make_config(state_dtype=state_dtype)
-    dt = sim.state_torch_dtype(cfg)
-    state = torch.full((2 * n + 16,), -1.5, dtype=dt, device=DEV)
+    ocfg = oracle_config(cfg)
+    rng = np.random.default_rng(n + 7 * state_dtype)
+    tail = 16
+    v = (rng.normal(size=2 * n + tail) * 10.0).astype(np.float32)
+    special = np.array([np.nan, np.inf, -np.inf, -0.0, 3e38, 1e-40], np.float32)
+    v[rng.integers(0, v.size, v.size // 4)] = rng.choice(special, v.size // 4)
+    garbage = O.f32_to_bf16_bits(v) if state_dtype == B.ECHO_STATE_BF16 else v
+    S, L = garbage[0:2 * n:2].copy(), garbage[1:2 * n:2].copy()
+    O.state_reset(S, L, ocfg)
+    ref = garbage.copy()
+    ref[:2 * n] = interleave(S, L)
+    state = state_dev(garbage)
     assert B.echo_state_bytes(n, state_dtype) == 2 * n * state.element_size()
     B.echo_state_reset(cfg, state, n)
     torch.cuda.synchronize()
-    h = host(state)[:2 * n]
-    assert not h.view(np.uint32 if h.dtype == np.float32 else np.uint16).any()
-    assert torch.all(state[2 * n:] == -1.5)
+    assert_bits_equal(host(state), ref, "reset state (and the words past it)")
+    assert not host(state)[:2 * n].view(np.uint32 if state_dtype == B.ECHO_STATE_F32 else np.uint16).any()
 
 
 # ------------------------------------------------------------------ whole call

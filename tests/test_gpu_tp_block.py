@@ -16,16 +16,24 @@ delivers), and with Echo (INT4, feedback gain 1, and gain 0 = no feedback).
 Each trajectory feeds its own h into its later branches.  Random weights only
 (no trained model).
 
+Every Echo call of the chain is also checked against the CPU oracle: the
+same bf16 partials go to the oracle's all-reduce with its own error state
+carried from site to site, and the output and every rank's short and long
+memories must agree bit for bit at every site, for gain 1 and gain 0.
+
 [JP] = 'テンソル並列の通信を4bitに圧縮する「Echo」——誤差補償で精度を保ちながら
 分散LLMを高速化する仕組み'.
 """
 import math
 
+import numpy as np
 import pytest
 import torch
 
+import oracle as O
 from error_compensated_bit_amd import binding as B
 from error_compensated_bit_amd import sim
+from echo_testutil import assert_bits_equal, host, oracle_config, split_state
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -56,6 +64,9 @@ def run_tp_chain(P=4, tokens=512, hidden=1024, sites=56, gain=1.0, norm=True, se
     hs = {k: h0.clone() for k in runs}
     ranks = {k: sim.alloc_ranks(B.make_config(eta=eta), P, n, DEV)
              for k, eta in runs.items() if eta is not None}
+    # the oracle's error state of every rank, carried from site to site
+    ostate = {k: ([np.zeros(n, np.float32) for _ in range(P)], [np.zeros(n, np.float32) for _ in range(P)])
+              for k, eta in runs.items() if eta is not None}
     dev = {k: [] for k in runs if k != "exact_fp32"}
     first_error = None
     for k in range(sites):
@@ -67,7 +78,17 @@ def run_tp_chain(P=4, tokens=512, hidden=1024, sites=56, gain=1.0, norm=True, se
         for name in ("echo_eta1", "echo_eta0"):
             ys = [y.to(torch.bfloat16).contiguous().reshape(-1) for y in partials(hs[name], W)]
             cfg = B.make_config(eta=runs[name])
-            out = sim.allreduce(cfg, ranks[name], ys).float().reshape(tokens, hidden)
+            r = ranks[name]
+            got = sim.allreduce(cfg, r, ys)
+            torch.cuda.synchronize()
+            oS, oL = ostate[name]
+            ref, _, _ = O.allreduce(oracle_config(cfg), [host(y) for y in ys], oS, oL)
+            assert_bits_equal(host(got), ref, f"{name} site {k} output")
+            for p in range(P):
+                S, L = split_state(r.state[p])
+                assert_bits_equal(S, oS[p], f"{name} site {k} rank {p} short memory")
+                assert_bits_equal(L, oL[p], f"{name} site {k} rank {p} long memory")
+            out = got.float().reshape(tokens, hidden)
             if first_error is None:
                 first_error = (out - sum(y.float() for y in ys).reshape(tokens, hidden)).pow(2).mean().sqrt().item()
             hs[name] = hs[name] + out
@@ -78,7 +99,8 @@ def run_tp_chain(P=4, tokens=512, hidden=1024, sites=56, gain=1.0, norm=True, se
 
 
 def report(tag, dev, q, sites):
-    print(f"[tp] {tag}: one call's injected error (rms) q = {q:.4g}")
+    print(f"[tp] {tag}: every Echo call matched the oracle bit for bit; "
+          f"one call's injected error (rms) q = {q:.4g}")
     for k in sorted({0, 3, 7, 15, sites - 1}):
         print(f"[tp]   after site {k + 1:2d}: echo eta=1 {dev['echo_eta1'][k] / q:9.3f} q   "
               f"eta=0 {dev['echo_eta0'][k] / q:9.3f} q   16-bit all-reduce "

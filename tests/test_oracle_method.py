@@ -300,6 +300,71 @@ def test_independent_errors_without_feedback_grow_as_sqrt_N():
     assert 0.8 * np.sqrt(sites) < growth < 1.2 * np.sqrt(sites)
 
 
+# --------------------------------------------------------------- state reset
+def garbage_state(rng, size, cfg):
+    """Memories holding leftovers of anything: NaN, +-Inf, -0, huge, subnormal
+    and ordinary values."""
+    v = (rng.normal(size=size) * 10.0).astype(np.float32)
+    special = np.array([np.nan, np.inf, -np.inf, -0.0, 3e38, -3e38, 1e-40, -1e-42], np.float32)
+    v[rng.integers(0, size, size // 4)] = rng.choice(special, size // 4)
+    if cfg.state_dtype == O.STATE_BF16:
+        return O.f32_to_bf16_bits(v)
+    return v
+
+
+@pytest.mark.parametrize("state_dtype", [O.STATE_F32, O.STATE_BF16])
+@pytest.mark.parametrize("n", [1, 7, 128, 1000])
+def test_state_reset_empties_both_memories(state_dtype, n):
+    """A chain of calls starts with both memories empty ([JP] 'Echoの仕組み②'
+    carries each call's error into later calls; the chain start is this
+    repository's reading): after the reset the first n elements of S and L
+    are +0 bit patterns (numpy's zeros of the state type), whatever they held,
+    and nothing past n is touched."""
+    cfg = O.Config(state_dtype=state_dtype)
+    rng = np.random.default_rng(n + 10 * state_dtype)
+    S = garbage_state(rng, n + 64, cfg)
+    L = garbage_state(rng, n + 64, cfg)
+    S0, L0 = S.copy(), L.copy()
+    O.state_reset(S, L, cfg, n)
+    zeros = np.zeros(n, O.state_np_dtype(cfg))
+    bits = np.uint32 if state_dtype == O.STATE_F32 else np.uint16
+    assert np.array_equal(S[:n].view(bits), zeros.view(bits))
+    assert np.array_equal(L[:n].view(bits), zeros.view(bits))
+    assert np.array_equal(S[n:].view(bits), S0[n:].view(bits))
+    assert np.array_equal(L[n:].view(bits), L0[n:].view(bits))
+
+
+@pytest.mark.parametrize("state_dtype", [O.STATE_F32, O.STATE_BF16])
+def test_reset_state_restarts_the_chain(state_dtype):
+    """Ranks whose state was reset after arbitrary earlier traffic continue
+    exactly like fresh ranks: every output, payload and state bit of three
+    chained calls equals the chain started from numpy zeros."""
+    cfg = O.Config(state_dtype=state_dtype)
+    P, n = 4, 4 * G * 3 + 200                     # ragged: a partial last group
+    rng = np.random.default_rng(77 + state_dtype)
+    seqs = [[rand_bf16(rng, n, t=4) for _ in range(P)] for _ in range(3)]
+    Sf, Lf = fresh_state(P, n, cfg)
+    Sr = [garbage_state(rng, n, cfg) for _ in range(P)]
+    Lr = [garbage_state(rng, n, cfg) for _ in range(P)]
+    for _ in range(2):                            # earlier calls on the garbage
+        O.allreduce(cfg, [rand_bf16(rng, n) for _ in range(P)], Sr, Lr)
+    for p in range(P):
+        O.state_reset(Sr[p], Lr[p], cfg)
+    for xs in seqs:
+        of, sf, wf = O.allreduce(cfg, xs, Sf, Lf)
+        orr, sr, wr = O.allreduce(cfg, xs, Sr, Lr)
+        assert np.array_equal(of, orr)
+        for o in range(P):
+            assert np.array_equal(wf[o][0], wr[o][0]) and np.array_equal(wf[o][1], wr[o][1])
+            for p in range(P):
+                if p != o:
+                    assert np.array_equal(sf[p][o][0], sr[p][o][0])
+                    assert np.array_equal(sf[p][o][1], sr[p][o][1])
+        for p in range(P):
+            assert np.array_equal(Sf[p].view(np.uint8), Sr[p].view(np.uint8))
+            assert np.array_equal(Lf[p].view(np.uint8), Lr[p].view(np.uint8))
+
+
 # --------------------------------------------------------------- storage variants
 def test_bf16_state_stores_the_rounded_fp32_update():
     """A compact state keeps bf16(RNE) of the value the fp32 state would hold;
