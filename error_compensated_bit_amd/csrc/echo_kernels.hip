@@ -418,7 +418,7 @@ __device__ __forceinline__ void entry_group(const uint16_t* __restrict__ x, void
 template <int BITS, int IN_T, int ST_T, int G, bool NT, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_quant_feedback(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable out, int rank,
-    FullGroups fg, uint64_t seg_len, Coef c) {
+    FullGroups fg, uint64_t seg_len, uint32_t bx0, Coef c) {
   using M = GroupMap<ST_T, G>;
   uint32_t bx = blockIdx.x, slot = blockIdx.y;
   if constexpr (XCD) {
@@ -426,6 +426,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_feedback(
     slot = L / gridDim.x;
     bx = L - slot * gridDim.x;
   }
+  bx += bx0;
   const uint32_t p = slot + ((int)slot >= rank ? 1u : 0u);
   const uint32_t lane = threadIdx.x % M::kLanes;
   const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
@@ -539,11 +540,11 @@ __device__ __forceinline__ void owner_group(const uint16_t* __restrict__ x, void
 template <int BITS, int IN_T, int ST_T, int OUT_T, int G, int NP, bool NT, bool NTP, bool XCD>
 __global__ __launch_bounds__(kThreads) void k_owner_reduce_requant(
     const uint16_t* __restrict__ x, void* __restrict__ state, SegTable in, int P, int rank,
-    FullGroups fg, uint64_t seg_len, uint8_t* __restrict__ out_codes,
+    FullGroups fg, uint64_t seg_len, uint32_t bx0, uint8_t* __restrict__ out_codes,
     uint32_t* __restrict__ out_params, Coef c) {
   using M = GroupMap<ST_T, G>;
   const uint32_t lane = threadIdx.x % M::kLanes;
-  const uint32_t bx = XCD ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
+  const uint32_t bx = (XCD ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x) + bx0;
   const uint32_t g = bx * M::kGroupsPerBlock + threadIdx.x / M::kLanes;
   if (g >= fg.of((uint32_t)rank)) return;
   owner_group<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, true>(x, state, in, P, rank, out_codes,
@@ -623,17 +624,19 @@ constexpr uint32_t gather_groups_per_block() {
 // and the partial group of a ragged message -- goes to k_dequant_gather_tail.
 template <int BITS, int OUT_T, int G, int CH, bool NT, bool NTP>
 __global__ __launch_bounds__(kThreads) void k_dequant_gather(SegTable in, FullGroups fg,
-                                                             uint64_t seg_len, void* __restrict__ out) {
+                                                             uint64_t seg_len, uint32_t bx0,
+                                                             void* __restrict__ out) {
   using M = GatherMap<OUT_T, G>;
   constexpr int EPL = M::kEPL;
   constexpr uint32_t kTile = gather_groups_per_block<OUT_T, G, CH>();
   const uint32_t p = blockIdx.y;
-  if (blockIdx.x >= fg.of(p) / kTile) return;   // whole block
+  const uint32_t bx = blockIdx.x + bx0;
+  if (bx >= fg.of(p) / kTile) return;   // whole block
   const uint8_t* __restrict__ codes = static_cast<const uint8_t*>(in.codes[p]);
   const uint32_t* __restrict__ params = in.params[p];
   const uint64_t base = (uint64_t)p * seg_len;
   const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const uint32_t g0 = (blockIdx.x * (kThreads / 64) + wave) * M::kGroupsPerWave * CH;
+  const uint32_t g0 = (bx * (kThreads / 64) + wave) * M::kGroupsPerWave * CH;
   const uint32_t in_group = (lane % M::kLanes) * EPL;
   u32x2 cw[CH];
   uint32_t pw[CH];
@@ -729,9 +732,24 @@ FullGroups full_groups(uint64_t n, uint64_t seg_len, int group) {
 }
 
 // Blocks along x: enough for every group, one group per lane run.
-unsigned blocks_for(uint64_t groups, uint64_t groups_per_block) {
+uint64_t blocks_for(uint64_t groups, uint64_t groups_per_block) {
   const uint64_t b = (groups + groups_per_block - 1) / groups_per_block;
-  return (unsigned)(b == 0 ? 1 : b);
+  return b == 0 ? 1 : b;
+}
+
+// A dispatch holds at most 2^32 - 1 work-items along x, so a grid of more
+// blocks than this goes out as several launches, each told the index of its
+// first block.  Only segments beyond about 2^33 elements need more than one.
+constexpr uint64_t kMaxBlocksX = 0xffffffffull / kThreads;
+
+// Launch blocks [0, blocks) along x as chunks of at most kMaxBlocksX; f(first,
+// count) makes one launch and returns its status.
+template <typename F>
+hipError_t in_chunks(uint64_t blocks, F&& f) {
+  hipError_t e = hipSuccess;
+  for (uint64_t b0 = 0; b0 < blocks && e == hipSuccess; b0 += kMaxBlocksX)
+    e = f((uint32_t)b0, (unsigned)(blocks - b0 < kMaxBlocksX ? blocks - b0 : kMaxBlocksX));
+  return e;
 }
 
 }  // namespace
@@ -754,10 +772,12 @@ template <int BITS, int IN_T, int ST_T, int G, bool NT, bool XCD>
 hipError_t launch_k1(const LaunchArgs& a, hipStream_t st) {
   const uint64_t groups = a.seg_len / G;
   const unsigned ny = (unsigned)(a.P - 1);
-  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock), ny);
-  hipError_t e = launch(k_quant_feedback<BITS, IN_T, ST_T, G, NT, XCD>, grid, dim3(kThreads), st,
-                        static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
-                        full_groups(a.n, a.seg_len, G), a.seg_len, a.coef);
+  hipError_t e = in_chunks(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock),
+                           [&](uint32_t b0, unsigned nb) {
+    return launch(k_quant_feedback<BITS, IN_T, ST_T, G, NT, XCD>, dim3(nb, ny), dim3(kThreads), st,
+                  static_cast<const uint16_t*>(a.x), a.state, a.segs, a.rank,
+                  full_groups(a.n, a.seg_len, G), a.seg_len, b0, a.coef);
+  });
   const Tail t = tail_of(a.n, a.seg_len, G);
   if (e == hipSuccess && t.valid && (int)t.p != a.rank)
     e = launch(k_quant_feedback_tail<BITS, IN_T, ST_T, G>, dim3(1), dim3(GroupMap<ST_T, G>::kLanes),
@@ -789,11 +809,13 @@ template <int BITS, int IN_T, int ST_T, int OUT_T, int G, int NP, bool NT, bool 
 hipError_t launch_k2(const LaunchArgs& a, hipStream_t st) {
   const uint64_t groups = a.seg_len / G;
   const SegTable in = owner_table(a);
-  dim3 grid(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock));
-  hipError_t e = launch(k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, XCD>, grid,
-                        dim3(kThreads), st, static_cast<const uint16_t*>(a.x), a.state, in, a.P,
-                        a.rank, full_groups(a.n, a.seg_len, G), a.seg_len,
-                        static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
+  hipError_t e = in_chunks(blocks_for(groups, GroupMap<ST_T, G>::kGroupsPerBlock),
+                           [&](uint32_t b0, unsigned nb) {
+    return launch(k_owner_reduce_requant<BITS, IN_T, ST_T, OUT_T, G, NP, NT, NTP, XCD>, dim3(nb),
+                  dim3(kThreads), st, static_cast<const uint16_t*>(a.x), a.state, in, a.P, a.rank,
+                  full_groups(a.n, a.seg_len, G), a.seg_len, b0,
+                  static_cast<uint8_t*>(a.out_codes), a.out_params, a.coef);
+  });
   const Tail t = tail_of(a.n, a.seg_len, G);
   if (e == hipSuccess && t.valid && (int)t.p == a.rank)
     e = launch(k_owner_reduce_requant_tail<BITS, IN_T, ST_T, OUT_T, G>, dim3(1),
@@ -810,8 +832,10 @@ hipError_t launch_k3(const LaunchArgs& a, hipStream_t st) {
   const Tail t = tail_of(a.n, a.seg_len, G);
   hipError_t e = hipSuccess;
   if (fg.all / tile > 0)
-    e = launch(k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>, dim3(fg.all / tile, a.P),
-               dim3(kThreads), st, a.segs, fg, a.seg_len, a.out);
+    e = in_chunks(fg.all / tile, [&](uint32_t b0, unsigned nb) {
+      return launch(k_dequant_gather<BITS, OUT_T, G, CH, NT, NTP>, dim3(nb, a.P), dim3(kThreads), st,
+                    a.segs, fg, a.seg_len, b0, a.out);
+    });
   if (e == hipSuccess && (fg.all % tile || fg.in_last % tile || t.valid))
     e = launch(k_dequant_gather_tail<BITS, OUT_T, G, CH>, dim3(1, a.P), dim3(kThreads), st, a.segs,
                fg, a.n, a.seg_len, a.out);

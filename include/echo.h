@@ -54,8 +54,14 @@
  *     default stream) and never synchronize.
  *   - Payload buffers must not overlap x, the state, the output or each other.
  *   - Every call validates all arguments before touching the GPU and
- *     returns ECHO_OK or a negative error code; nothing is launched when an
- *     error is returned.  No exception crosses this interface.
+ *     returns ECHO_OK or a negative error code.  ECHO_ERR_ARG, ECHO_ERR_SHAPE
+ *     and ECHO_ERR_ALIGN are returned before anything is launched.  A call
+ *     may make more than one launch (the one partial group of a ragged
+ *     message runs in a launch of its own, and a segment of more than about
+ *     2^33 elements is split over several); ECHO_ERR_HIP can therefore come
+ *     after some launches of the call went out, and the state and payloads
+ *     it writes may then be partly updated: reset (or restore) the state
+ *     before the next call.  No exception crosses this interface.
  */
 #ifndef ECHO_H
 #define ECHO_H
@@ -73,7 +79,8 @@ extern "C" {
 #define ECHO_ERR_SHAPE  -2   /* n <= 0, or a segment of more than 2^31 groups
                                 (every n > 2^48 is one) */
 #define ECHO_ERR_ALIGN  -3   /* a buffer pointer is not 16-byte aligned */
-#define ECHO_ERR_HIP    -4   /* the HIP runtime reported an error at launch */
+#define ECHO_ERR_HIP    -4   /* the HIP runtime reported an error at a launch (earlier
+                                launches of the same call may have gone out) */
 
 /* element types */
 #define ECHO_IN_BF16     0   /* 16-bit input message: bfloat16 */
