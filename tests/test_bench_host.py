@@ -44,15 +44,31 @@ def test_bench_refuses_more_than_one_gpu():
     assert "--gpus 1" in r.stderr
 
 
-def test_traffic_is_reported_only_for_the_profiled_configuration():
-    """profiles/ holds counters for the default launch (fp32 state, group
-    128, rank 0); another configuration of the same workload reports none."""
-    cfg = dict(bench.PROFILED_CONFIG)
-    t = bench.traffic_from_profile("msg1gib_p8", "k_quant_feedback", cfg)
-    if t is None:
-        import pytest
+def test_traffic_is_reported_only_for_a_profiled_configuration():
+    """Each pmc summary in profiles/ covers one workload and launch
+    configuration; a configuration no summary covers reports no traffic."""
+    import glob
+    import json
+    import pytest
+    found = 0
+    for path in glob.glob(os.path.join(ROOT, "profiles", "pmc_*.json")):
+        d = json.load(open(path))
+        if d.get("kernel_source_digest") != bench.kernel_source_digest():
+            continue
+        cfg = {**bench.DEFAULT_CONFIG, **d["config"]}
+        assert os.path.basename(path) == f"pmc_{bench.profile_key(d['workload'], cfg)}.json"
+        t = bench.traffic_from_profile(d["workload"], "k_quant_feedback", cfg)
+        assert t is not None
+        found += 1
+        for change in ({"group": 32}, {"rank": 5}, {"site": 77}):
+            assert bench.traffic_from_profile(d["workload"], "k_quant_feedback", {**cfg, **change}) is None
+    if not found:
         pytest.skip("no profile for the current kernel source")
-    alg = bench.algorithmic_bytes(8, 536870912, 4, 4)["k_quant_feedback"]
-    assert 0.99 < t / alg < 1.05
-    for change in ({"state": "bf16"}, {"group": 64}, {"rank": 3}, {"site": 5}):
-        assert bench.traffic_from_profile("msg1gib_p8", "k_quant_feedback", {**cfg, **change}) is None
+
+
+def test_profile_key_names_only_non_default_settings():
+    assert bench.profile_key("msg1gib_p8", dict(bench.DEFAULT_CONFIG)) == "msg1gib_p8"
+    assert bench.profile_key("msg1gib_p8", {**bench.DEFAULT_CONFIG, "state": "bf16"}) == "msg1gib_p8_state-bf16"
+    assert bench.profile_key("mixed_p8_16384x5120", {"site": 20}) == "mixed_p8_16384x5120_site-20"
+    cmds = bench.profile_commands("mixed_p8_16384x5120", {"site": 20})
+    assert all("--site 20" in c for k, c in cmds.items() if not k.startswith("copy"))
