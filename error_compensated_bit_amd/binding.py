@@ -186,3 +186,50 @@ def echo_dequant_gather(cfg: echo_config, P: int, n: int, inp, out: torch.Tensor
     _check(load_library().echo_dequant_gather(ctypes.byref(cfg), P, n, _seg_table(P, inp),
                                               _ptr(out), _stream(stream)),
            "echo_dequant_gather")
+
+
+class Prepared:
+    """One entry-point call with every argument marshalled once (config,
+    payload tables, pointers and stream): calling it makes only the foreign
+    call.  For callers that repeat the same call on the same buffers, where
+    marshalling would cost more host time than a small message's kernels.
+    The buffers must stay alive and in place while it is used."""
+
+    def __init__(self, fn, args, keep, where: str):
+        self._fn = fn
+        self._args = args
+        self._keep = keep          # the ctypes objects the byref arguments point at
+        self._where = where
+
+    def __call__(self):
+        rc = self._fn(*self._args)
+        if rc != ECHO_OK:
+            raise EchoError(rc, self._where)
+
+
+def prepare_quantize_feedback(cfg: echo_config, P: int, rank: int, n: int, x: torch.Tensor,
+                              state: torch.Tensor, out, stream=None) -> Prepared:
+    L = load_library()
+    c = echo_config(*(getattr(cfg, f) for f, _ in echo_config._fields_))
+    return Prepared(L.echo_quantize_feedback,
+                    (ctypes.byref(c), P, rank, n, _ptr(x), _ptr(state), _seg_table(P, out),
+                     _stream(stream)), c, "echo_quantize_feedback")
+
+
+def prepare_owner_reduce_requant(cfg: echo_config, P: int, rank: int, n: int, x: torch.Tensor,
+                                 state: torch.Tensor, inp, out: Payload, stream=None) -> Prepared:
+    L = load_library()
+    c = echo_config(*(getattr(cfg, f) for f, _ in echo_config._fields_))
+    out_seg = out.seg()
+    return Prepared(L.echo_owner_reduce_requant,
+                    (ctypes.byref(c), P, rank, n, _ptr(x), _ptr(state), _seg_table(P, inp),
+                     ctypes.byref(out_seg), _stream(stream)), (c, out_seg), "echo_owner_reduce_requant")
+
+
+def prepare_dequant_gather(cfg: echo_config, P: int, n: int, inp, out: torch.Tensor,
+                           stream=None) -> Prepared:
+    L = load_library()
+    c = echo_config(*(getattr(cfg, f) for f, _ in echo_config._fields_))
+    return Prepared(L.echo_dequant_gather,
+                    (ctypes.byref(c), P, n, _seg_table(P, inp), _ptr(out), _stream(stream)), c,
+                    "echo_dequant_gather")

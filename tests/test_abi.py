@@ -145,3 +145,21 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "library_path", lambda: str(tmp_path / "libecho_amd.so"))
     with pytest.raises(RuntimeError, match="build"):
         binding.load_library()
+
+
+def test_prepared_call_reports_the_code_of_its_call():
+    """A prepared (pre-marshalled) call runs the same validation on every
+    call: an invalid configuration raises with ECHO_ERR_ARG before any HIP
+    call, each time it is called."""
+    import torch
+    x = torch.zeros(256, dtype=torch.int16)
+    st = torch.zeros(512, dtype=torch.float32)
+    pay = B.Payload(torch.zeros(64, dtype=torch.uint8), torch.zeros(1, dtype=torch.int32))
+    bad = B.make_config(bits=5)
+    for prep in (B.prepare_quantize_feedback(bad, 2, 0, 256, x, st, [None, pay], stream=0),
+                 B.prepare_owner_reduce_requant(bad, 2, 0, 256, x, st, [None, pay], pay, stream=0),
+                 B.prepare_dequant_gather(bad, 2, 256, [pay, pay], x, stream=0)):
+        for _ in range(2):
+            with pytest.raises(B.EchoError) as e:
+                prep()
+            assert e.value.code == B.ECHO_ERR_ARG
