@@ -193,7 +193,8 @@ class Prepared:
     payload tables, pointers and stream): calling it makes only the foreign
     call.  For callers that repeat the same call on the same buffers, where
     marshalling would cost more host time than a small message's kernels.
-    The buffers must stay alive and in place while it is used."""
+    It holds references to every tensor it was given, so they stay allocated
+    while it exists; it always launches on the stream it was prepared with."""
 
     def __init__(self, fn, args, keep, where: str):
         self._fn = fn
@@ -213,7 +214,7 @@ def prepare_quantize_feedback(cfg: echo_config, P: int, rank: int, n: int, x: to
     c = echo_config(*(getattr(cfg, f) for f, _ in echo_config._fields_))
     return Prepared(L.echo_quantize_feedback,
                     (ctypes.byref(c), P, rank, n, _ptr(x), _ptr(state), _seg_table(P, out),
-                     _stream(stream)), c, "echo_quantize_feedback")
+                     _stream(stream)), (c, x, state, list(out)), "echo_quantize_feedback")
 
 
 def prepare_owner_reduce_requant(cfg: echo_config, P: int, rank: int, n: int, x: torch.Tensor,
@@ -223,7 +224,8 @@ def prepare_owner_reduce_requant(cfg: echo_config, P: int, rank: int, n: int, x:
     out_seg = out.seg()
     return Prepared(L.echo_owner_reduce_requant,
                     (ctypes.byref(c), P, rank, n, _ptr(x), _ptr(state), _seg_table(P, inp),
-                     ctypes.byref(out_seg), _stream(stream)), (c, out_seg), "echo_owner_reduce_requant")
+                     ctypes.byref(out_seg), _stream(stream)), (c, out_seg, x, state, list(inp), out),
+                    "echo_owner_reduce_requant")
 
 
 def prepare_dequant_gather(cfg: echo_config, P: int, n: int, inp, out: torch.Tensor,
@@ -231,5 +233,5 @@ def prepare_dequant_gather(cfg: echo_config, P: int, n: int, inp, out: torch.Ten
     L = load_library()
     c = echo_config(*(getattr(cfg, f) for f, _ in echo_config._fields_))
     return Prepared(L.echo_dequant_gather,
-                    (ctypes.byref(c), P, n, _seg_table(P, inp), _ptr(out), _stream(stream)), c,
-                    "echo_dequant_gather")
+                    (ctypes.byref(c), P, n, _seg_table(P, inp), _ptr(out), _stream(stream)),
+                    (c, list(inp), out), "echo_dequant_gather")
