@@ -9,6 +9,11 @@
     sampled groups of every segment (every group is independent of the
     others, also across calls, because the state is per element), and the
     two are compared bit for bit on those groups.
+  * the 56-call chain again with the compact bf16 error state, every element;
+  * the feedback's bound re-checked on the GPU's own outputs over that chain.
+
+[JP] = 'テンソル並列の通信を4bitに圧縮する「Echo」——誤差補償で精度を保ちながら
+分散LLMを高速化する仕組み'.
 """
 import numpy as np
 import pytest
@@ -133,3 +138,53 @@ def test_1gib_call_then_benchmark_share(state_dtype):
     sent2 = [new_sent0] + sent[1:]
     compare_call(cfg, r, groups, idx, out2, sent2, owned2, oS, oL, "benchmark share", (0,))
     torch.cuda.synchronize()
+
+
+def test_chain56_p4_bf16_state_every_element():
+    """The depth chain with the compact bf16 error state: every element of
+    every output, payload and state of all 56 calls."""
+    w = WORKLOADS["chain56_p4_512x1024"]
+    banner(w.description + " bf16 state")
+    run_chain(w, lambda s: B.make_config(state_dtype=B.ECHO_STATE_BF16), 0, 0, full=True,
+              state_ranks=range(w.P))
+
+
+def gpu_chain_errors(w, cfg, inputs):
+    """Run a chain of len(inputs) calls on the GPU from an empty state and
+    return, per call, o - sum_p x_p and the feedback sum sum_p (S + L) held
+    before the call (fp64, elementwise), read from the device."""
+    P, n = w.P, w.n
+    r = sim.alloc_ranks(cfg, P, n, DEV)
+    d, F = [], []
+    for xs in inputs:
+        fb = np.zeros(n)
+        for p in range(P):
+            st = r.state[p].double().cpu().numpy()
+            fb += st[0::2] + st[1::2]
+        out = sim.allreduce(cfg, r, xs)
+        torch.cuda.synchronize()
+        d.append(out.double().cpu().numpy() - sum(x.double().cpu().numpy() for x in xs))
+        F.append(fb)
+    return np.array(d), np.array(F)
+
+
+def test_feedback_bound_on_gpu_outputs():
+    """The pages' claims re-checked on the GPU's own outputs over the 56-call
+    chain ([JP] '理論保証', 'なぜ4bit通信は難しかったのか'): with gain 1 the
+    accumulated error A_N = sum_k (o_k - sum_p x_pk) stays within 2.1 times
+    the largest single-call error e_k = o_k - sum_p (x_pk + S + L) at every
+    depth and element; without feedback the same input repeated injects the
+    same error every call, so A_N = N e_1 exactly."""
+    w = WORKLOADS["chain56_p4_512x1024"]
+    banner("feedback bound on GPU outputs")
+    seqs = [[make_x(w, s, p, device=DEV) for p in range(w.P)] for s in range(w.sites)]
+    d, F = gpu_chain_errors(w, B.make_config(eta=1.0), seqs)
+    e = d - F
+    A = np.cumsum(d, axis=0)
+    q = np.abs(e).max(axis=0)
+    assert np.all(np.abs(A) <= 2.1 * q * (1 + 1e-5) + 1e-30)
+    d0, _ = gpu_chain_errors(w, B.make_config(eta=0.0), [seqs[0]] * w.sites)
+    assert np.all(d0 == d0[0])
+    A0 = np.cumsum(d0, axis=0)
+    assert np.array_equal(A0[-1], w.sites * d0[0])
+    assert np.abs(A0[-1]).mean() > 10 * np.abs(A[-1]).mean()
