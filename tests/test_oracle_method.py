@@ -250,6 +250,50 @@ def test_accumulated_error_follows_the_feedback_filter(eta):
         assert np.abs(A[N - 1] - pred).max() <= 1e-5 * scale, N
 
 
+def chain_identity_residual(cfg, seqs, fault=None, at=None):
+    """Run a chain of calls on the oracle, optionally with a fault at call
+    `at`: "skip" discards that call's state update (the memories are put back
+    as they were), "repeat" runs that call twice while counting its output
+    once.  Returns the largest deviation of A_N from the filter prediction
+    over all depths, relative to the largest injected error."""
+    P, n = len(seqs[0]), seqs[0][0].size
+    Ss, Ls = fresh_state(P, n, cfg)
+    d, F = [], []
+    for k, xs in enumerate(seqs):
+        F.append(sum(S.astype(np.float64) + Lm.astype(np.float64) for S, Lm in zip(Ss, Ls)))
+        keep = [(S.copy(), Lm.copy()) for S, Lm in zip(Ss, Ls)]
+        if fault == "repeat" and k == at:
+            O.allreduce(cfg, xs, Ss, Ls)
+        out, _, _ = O.allreduce(cfg, xs, Ss, Ls)
+        if fault == "skip" and k == at:
+            for p, (S0, L0) in enumerate(keep):
+                Ss[p][:] = S0
+                Ls[p][:] = L0
+        d.append(out_to_f64(out, cfg) - sum(bf16_to_f64(x) for x in xs))
+    d, F = np.array(d), np.array(F)
+    e = d - cfg.eta * F
+    A = np.cumsum(d, axis=0)
+    worst = 0.0
+    for N in range(1, len(seqs) + 1):
+        c = np.array([1 - cfg.eta * (1 - filter_weights(cfg, N - 1 - k)) for k in range(N)])
+        worst = max(worst, np.abs(A[N - 1] - (c[:, None] * e[:N]).sum(axis=0)).max())
+    return worst / np.abs(e).max()
+
+
+@pytest.mark.parametrize("fault", ["skip", "repeat"])
+def test_filter_identity_detects_a_skipped_or_repeated_call(fault):
+    """The accumulated error follows the feedback filter only if every call
+    updates the state exactly once ([JP] 'Echoの仕組み②'): a call whose state
+    update is lost, or a call run twice, breaks the identity by far more than
+    its rounding tolerance, so checking it detects either fault."""
+    cfg = O.Config()
+    P, n, sites = 4, 4 * G * 4, 12
+    rng = np.random.default_rng(45)
+    seqs = [[rand_bf16(rng, n, t=4) for _ in range(P)] for _ in range(sites)]
+    assert chain_identity_residual(cfg, seqs) <= 1e-5
+    assert chain_identity_residual(cfg, seqs, fault, at=5) > 1e-2
+
+
 def test_bound_with_gain_one():
     """With eta = 1 the accumulated error stays within the stated factor of
     the per-call error at every depth; the filter's total weight
