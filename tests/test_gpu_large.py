@@ -119,9 +119,10 @@ def test_owner_pass_split_over_two_launches():
     groups = split_groups(gps, np.random.default_rng(99))
     idx = group_index(P, n, groups)
     print(f"[gpu] owner pass over two launches: n={n}, {groups.size} groups compared", flush=True)
-    r = sim.alloc_ranks(cfg, P, n, DEV)
+    r = None
     oS, oL = [np.zeros(idx.size, np.float32)], [np.zeros(idx.size, np.float32)]
     try:
+        r = sim.alloc_ranks(cfg, P, n, DEV)
         for call in range(2):
             x = random_bf16(n, 5000 + call)
             sim.allreduce(cfg, r, [x])
@@ -157,9 +158,10 @@ def test_entry_pass_split_over_two_launches():
     groups = split_groups(gps, np.random.default_rng(98))
     idx = group_index(P, seg, groups)
     print(f"[gpu] entry pass over two launches: n={n}, {groups.size} groups per segment", flush=True)
-    state = torch.empty(2 * n, dtype=torch.float32, device=DEV)
-    pay = B.alloc_payload(seg, cfg.bits, DEV)
+    state = pay = None
     try:
+        state = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+        pay = B.alloc_payload(seg, cfg.bits, DEV)
         B.echo_state_reset(cfg, state, n)
         x = random_bf16(n, 6000)
         B.echo_quantize_feedback(cfg, P, 0, n, x, state, [None, pay])
